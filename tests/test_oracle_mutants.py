@@ -1,0 +1,122 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the
+pins catch each one.  This shows the pins constrain the oracle rather than
+restate it."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import fp8
+from tests import test_oracle_attention as TA
+from tests import test_oracle_fp8 as TF
+
+
+def _sdpa_pin():
+    q, dk, dv, kc, vc, tab, L = TA._case(21, [1, 17, 40], 8, 2, 16, 16)
+    ours = A.paged_decode(q, kc, vc, tab, L, 0.25, 16)
+    ref = TA._sdpa(q, dk, dv, 8, 2, 0.25)
+    np.testing.assert_allclose(ours, ref, rtol=1e-12, atol=1e-13)
+
+
+def _online_pin():
+    q, dk, dv, kc, vc, tab, L = TA._case(22, [100], 2, 1, 16, 16)
+    o1 = A.paged_decode(q, kc, vc, tab, L, 0.3, 16)
+    got = A.online_decode_one(q[0, 0], kc, vc, tab[0], 100, 0.3, 16, 0)
+    np.testing.assert_allclose(got, o1[0, 0], rtol=1e-12, atol=1e-13)
+
+
+def _merge_pin():
+    q, dk, dv, kc, vc, tab, L = TA._case(23, [300], 1, 1, 8, 16)
+    o1 = A.paged_decode(q, kc, vc, tab, L, 0.3, 16)
+    got = A.partitioned_decode_one(q[0, 0], dk[0][:, 0], dv[0][:, 0], 0.3,
+                                   A.split_points(300, 64))
+    np.testing.assert_allclose(got, o1[0, 0], rtol=1e-12, atol=1e-13)
+
+
+def _wrong_kv_head(h, g):
+    return h % 2            # interleaved instead of grouped
+
+
+def _wrong_address(table_row, t, bs):
+    t = np.asarray(t, dtype=np.int64)
+    return np.asarray(table_row)[t // bs], (t + 1) % bs
+
+
+def _no_scale(q, K, V, scale):
+    s = K @ q
+    w = np.exp(s - s.max())
+    return (w @ V) / w.sum()
+
+
+def _transposed_scores(q, K, V, scale):
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    return (w @ V[::-1]) / w.sum()
+
+
+def _printed_online(q, key_cache, value_cache, table_row, L, scale, bs, kvh):
+    # the listing's update, applied literally: acc *= l_rescaled * alpha
+    m, l, acc = -np.inf, 0.0, np.zeros(q.shape[0])
+    for i in range(-(-L // bs)):
+        phys = int(table_row[i]); valid = min(bs, L - i * bs)
+        s = scale * (key_cache[phys, :valid, kvh] @ q)
+        m_new = max(m, float(s.max()))
+        l = l * math.exp(m - m_new)
+        p = np.exp(s - m_new)
+        acc = acc * l * math.exp(m - m_new) + p @ value_cache[phys, :valid, kvh]
+        l += p.sum(); m = m_new
+    return acc / l
+
+
+def _unweighted_merge(triples):
+    M = max(t[0] for t in triples)
+    return sum(t[2] * np.exp(t[0] - M) for t in triples) / len(triples)
+
+
+@pytest.mark.parametrize("target,attr,mutant,pin", [
+    (A, "kv_head_for", _wrong_kv_head, _sdpa_pin),
+    (A, "token_address", _wrong_address, _sdpa_pin),
+    (A, "softmax_attend", _no_scale, _sdpa_pin),
+    (A, "softmax_attend", _transposed_scores, _sdpa_pin),
+    (A, "online_decode_one", _printed_online, _online_pin),
+    (A, "merge_triples", _unweighted_merge, _merge_pin),
+])
+def test_attention_mutants_are_caught(monkeypatch, target, attr, mutant, pin):
+    pin()                                   # passes on the real oracle
+    monkeypatch.setattr(target, attr, mutant)
+    with pytest.raises((AssertionError, IndexError)):
+        pin()
+
+
+def _ties_away(y):
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    pos = fp8._POS
+    hi = np.minimum(np.searchsorted(pos, a), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    code = np.where(np.abs(pos[hi] - a) <= np.abs(a - pos[lo]), hi, lo)
+    code = np.where(a >= 448, 0x7E, code)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+_REAL_TABLE = fp8.decode_table
+
+
+def _bias8_table():
+    return _REAL_TABLE() / 2.0
+
+
+def test_fp8_round_mutant_is_caught(monkeypatch):
+    TF.test_round_matches_torch_on_edges()
+    monkeypatch.setattr(fp8, "round_to_e4m3", _ties_away)
+    with pytest.raises(AssertionError):
+        TF.test_round_matches_torch_on_edges()
+
+
+def test_fp8_table_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(fp8, "decode_table", _bias8_table)
+    with pytest.raises(AssertionError):
+        TF.test_decode_table_matches_torch()
