@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step = the whole decode hot path over one batch: write each sequence's
+new K/V token into its cache slot (pa_reshape_and_cache), then single-query
+attention of every query head over its sequence's paged K/V
+(pa_decode: partition kernel, plus the merge kernel when the plan splits).
+Inputs are synthetic and seeded (synth/), resident in HBM before timing.
+
+Prints ONE JSON line:
+  value           KV GB/s over the whole timed step (algorithmic KV bytes of
+                  the batch / step time)
+  roofline        the decode call measured with HIP events on the launch
+                  stream: algorithmic KV bytes per launch / mean duration,
+                  against the 8 TB/s HBM peak; `traffic` from the committed
+                  rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken
+                  from the current kernel source, else null
+  cpu_baseline    the CPU oracle (fp64) on a bounded sample of the same
+                  batch, on this host's cores, for context only
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention: achieved KV HBM GB/s (% of peak) and tokens/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_462_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, launch_desc: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current decode kernel source and launch plan."""
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash() or t.get("launch") != launch_desc:
+        return None
+    return t
+
+
+def cpu_baseline(wl, seconds: float):
+    """The oracle, unchanged, over the first sequences of the batch until the
+    time budget is spent."""
+    import numpy as np
+
+    from oracle import attention as OA
+    from oracle import cache_write as OW
+    from synth.generate import empty_cache_cpu
+
+    kc, vc = empty_cache_cpu(wl), empty_cache_cpu(wl)
+    OW.reshape_and_cache(wl.tok_key, wl.tok_value, wl.slot_mapping, kc, vc,
+                         wl.cfg.kv_dtype, wl.k_scale, wl.v_scale)
+    c = wl.cfg
+    done, t_used, kv_bytes = 0, 0.0, 0
+    esz = wl.kv_bytes_per_elem()
+    for b in range(c.batch):
+        pairs = [(b, h) for h in range(c.num_q_heads)]
+        t0 = time.perf_counter()
+        OA.paged_decode_stored(wl.query, kc, vc, c.kv_dtype, wl.k_scale, wl.v_scale,
+                               wl.block_tables, wl.seq_lens, wl.scale, c.block_size, pairs)
+        t_used += time.perf_counter() - t0
+        done += 1
+        kv_bytes += int(wl.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * esz
+        if t_used >= seconds:
+            break
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    import torch
+    threads = max(threads, torch.get_num_threads())
+    return {
+        "value": round(kv_bytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of sequences 0..{done - 1} of {c.batch} "
+                  f"(all {c.num_q_heads} query heads, {kv_bytes / 1e6:.1f} MB of KV) in "
+                  f"{t_used:.2f} s; tokens/s {done / t_used:.2f}",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", help="workload name or c1..c5 (default: the 7B-shaped decode)")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--flushed-iters", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path shards by kv head or by sequence with no exchange inside attention, "
+              "and multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_462_amd as pa
+    from synth import get_config, make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    cfg = get_config(args.config)
+    log(f"[bench] generating {cfg.name}")
+    wl = make_workload(cfg)
+    dev = torch.device("cuda:0")
+    c = wl.cfg
+    fp8 = c.kv_dtype == "fp8"
+    kvd = "fp8" if fp8 else None
+    shape = (wl.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    st = torch.uint8 if fp8 else wl.tok_key.dtype
+    kc = torch.zeros(shape, dtype=st, device=dev)
+    vc = torch.zeros(shape, dtype=st, device=dev)
+    q = wl.query.to(dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.seq_lens).to(dev)
+    # fill the cache once (set-up, untimed)
+    pa.reshape_and_cache(wl.tok_key.to(dev), wl.tok_value.to(dev),
+                         torch.from_numpy(wl.slot_mapping).to(dev), kc, vc,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
+    new_k = wl.new_key().to(dev)
+    new_v = wl.new_value().to(dev)
+    new_slots = torch.from_numpy(wl.new_slots).to(dev)
+    out = torch.empty_like(q)
+    ws_bytes = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                         c.block_size, wl.max_blocks, args.partition_tokens)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    part = pa.decode_plan_partition(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                    c.block_size, wl.max_blocks, args.partition_tokens)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def decode():
+        pa.decode(out, q, kc, vc, tables, lens, wl.scale, c.block_size, c.num_kv_heads,
+                  k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, workspace=ws,
+                  partition_tokens=args.partition_tokens, path=args.path)
+
+    def step():
+        pa.reshape_and_cache(new_k, new_v, new_slots, kc, vc, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale, kv_dtype=kvd)
+        decode()
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        pa.reshape_and_cache(new_k, new_v, new_slots, kc, vc, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale, kv_dtype=kvd)
+        evs[i][0].record(stream)
+        decode()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_mean = float(np.mean(dec_ms))
+    dec_med = float(np.median(dec_ms))
+
+    # decode with L2 and MALL flushed before every launch (1 GiB written)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    fl_ms = []
+    for _ in range(args.flushed_iters):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        decode()
+        b.record(stream)
+        b.synchronize()
+        fl_ms.append(a.elapsed_time(b))
+    del flush
+    fl_med = float(np.median(fl_ms)) if fl_ms else None
+
+    kv_unique = wl.unique_kv_bytes()
+    kv_logical = wl.logical_kv_bytes()
+    gbps_step = kv_unique / (ms_step * 1e-3) / 1e9
+    achieved = kv_unique / (dec_mean * 1e-3) / 1e9
+    launch_desc = f"partition={part} path={args.path}"
+    traffic = load_traffic(c.name, launch_desc)
+    roof = {
+        "bound": "hbm",
+        "kernel": "pa_decode" + (" (partition + merge kernels)" if part else ""),
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None),
+        "algorithmic_bytes_per_launch": kv_unique,
+        "mean_launch_ms": round(dec_mean, 5),
+        "median_launch_ms": round(dec_med, 5),
+        "flushed_median_launch_ms": round(fl_med, 5) if fl_med else None,
+        "flushed_GBps": round(kv_unique / (fl_med * 1e-3) / 1e9, 1) if fl_med else None,
+    }
+    res = {
+        "metric": METRIC,
+        "value": round(gbps_step, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.kv_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": c.name,
+            "batch": c.batch,
+            "num_q_heads": c.num_q_heads,
+            "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim,
+            "block_size": c.block_size,
+            "seq_lens": list(map(str, c.lengths)),
+            "sum_seq_len": int(wl.seq_lens.astype(np.int64).sum()),
+            "q_dtype": c.q_dtype,
+            "kv_dtype": c.kv_dtype,
+            "partition_tokens": part,
+            "path": {0: "auto", 1: "valu", 2: "mfma"}[args.path],
+            "kv_bytes_unique": kv_unique,
+            "kv_bytes_logical": kv_logical,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(c.batch / (ms_step * 1e-3), 1),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds}s)")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,241 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged decode-attention library.
+ *
+ * The operation: single-query decode attention over a paged KV cache.  K and
+ * V live in fixed-size physical blocks shaped
+ * [num_blocks, block_size, num_kv_heads, head_dim]; each sequence reaches its
+ * tokens through a row of a block table that maps logical block i (tokens
+ * [i*block_size, (i+1)*block_size)) to a physical block id.  Defined by the
+ * pages:
+ *   "paged-attention-and-vllm-inference" (astro-blog-cod.pages.dev), code
+ *     block `paged_attention` (block-table indirection, partly filled last
+ *     block, running max / running sum with rescale) and the kernel design
+ *     points block (block table resident on the device, per-sequence lengths);
+ *   "5.KV Cache 管理 & PagedAttention" (lowentro.cn), question 7 (GQA/MQA:
+ *     a kv head serves Hq/Hkv consecutive query heads), question 8 (batch
+ *     block table [B, max_blocks] int32 padded with -1, plus per-sequence
+ *     lengths), question 9 (block allocator, reference counts), question 12
+ *     (writing a new token at block = pos / bs, offset = pos % bs),
+ *     question 13 (per-block loads inside the kernel), question 18
+ *     (copy-on-write of a shared block), question 20 (shared prefix blocks);
+ *   "KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践"
+ *     (aiattnstudio.link), `PagedAttentionKernel.kernel_design` (kernel
+ *     arguments: query, caches, block_tables, seq_lens, output, block size).
+ *
+ * Conventions shared by every call
+ *   - Tensors are passed as `pa_tensor` descriptors: a device address, a
+ *     dtype, a rank, a shape and strides in elements.  The caller allocates
+ *     and owns every device buffer; the library never allocates, frees or
+ *     synchronises device memory.
+ *   - Device work is enqueued asynchronously on `launch->stream` (a
+ *     hipStream_t; NULL means the null stream).  A call returns once its
+ *     kernels are enqueued.
+ *   - Every argument is validated on the host before any HIP call, so a bad
+ *     call fails with PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED / PA_ERR_WORKSPACE
+ *     and touches no device state.  Device-resident contents (block ids,
+ *     lengths, slots) are trusted: block ids must lie in [0, num_blocks),
+ *     seq_lens[b] <= max_blocks * block_size, slots must be unique and inside
+ *     the cache.
+ *   - Every call returns PA_OK (0) or a negative status; pa_last_error()
+ *     then holds a message (thread-local, valid until the next call on the
+ *     same thread).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PA_OK 0
+#define PA_ERR_INVALID_ARG (-1)   /* bad shape, stride, dtype, null pointer   */
+#define PA_ERR_WORKSPACE (-2)     /* split decode needs a larger workspace     */
+#define PA_ERR_OUT_OF_BLOCKS (-3) /* allocator has no free block               */
+#define PA_ERR_BAD_BLOCK (-4)     /* id out of range, not allocated, underflow */
+#define PA_ERR_HIP (-5)           /* a HIP launch reported an error            */
+#define PA_ERR_UNSUPPORTED (-6)   /* valid request outside the built variants  */
+#define PA_ERR_NOT_FOUND (-7)     /* unknown sequence id                       */
+
+/* element types */
+#define PA_F32 0
+#define PA_F16 1
+#define PA_BF16 2
+#define PA_FP8_E4M3 3 /* OCP E4M3FN, stored as one byte */
+#define PA_I32 4
+#define PA_I64 5
+
+typedef struct pa_tensor {
+  void* data;        /* device address, owned by the caller                    */
+  int32_t dtype;     /* PA_F32 ... PA_I64                                      */
+  int32_t ndim;      /* 1..4                                                   */
+  int64_t shape[4];  /* extents, outermost first                               */
+  int64_t stride[4]; /* strides in elements                                    */
+  float scale;       /* fp8 tensors: stored value = decoded code * scale       */
+} pa_tensor;
+
+/* decode path selection (tests and tuning; 0 = automatic) */
+#define PA_PATH_AUTO 0
+#define PA_PATH_VALU 1 /* per-lane dot products, DPP reductions             */
+#define PA_PATH_MFMA 2 /* query-group x K-tile and P x V on matrix cores    */
+
+typedef struct pa_launch {
+  void* stream;             /* hipStream_t; NULL = null stream                   */
+  void* workspace;          /* device scratch for split decode, caller-owned     */
+  size_t workspace_bytes;   /* its size                                          */
+  int32_t partition_tokens; /* 0 = automatic; -1 = never split; > 0: split each
+                               sequence into partitions of this many tokens
+                               (a multiple of 16)                                */
+  int32_t path;             /* PA_PATH_*                                         */
+} pa_launch;
+
+/*
+ * pa_reshape_and_cache -- write new K/V tokens into their cache slots.
+ *   key, value    [T, Hkv, D]   f32 | f16 | bf16; token stride free, the head
+ *                               stride and the dim stride must be D and 1
+ *   slot_mapping  [T]           i64; slot = block * block_size + offset;
+ *                               a negative slot skips that token
+ *   key_cache,
+ *   value_cache   [N, bs, Hkv, D] contiguous; same dtype as key/value (bit
+ *                               copy), or PA_FP8_E4M3: code = E4M3(x / scale)
+ *                               with one fp32 division, round to nearest even,
+ *                               saturating at +-448, NaN kept (the cache
+ *                               tensor's `scale` is the per-tensor scale)
+ *   launch        stream (workspace unused); NULL = null stream
+ * Two tokens of one call must not share a slot (the written value is then
+ * unspecified).  T = 0 is a no-op.
+ */
+int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
+                         const pa_tensor* slot_mapping, pa_tensor* key_cache,
+                         pa_tensor* value_cache, const pa_launch* launch);
+
+/*
+ * pa_decode -- out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b, where K_b, V_b
+ * are the first seq_lens[b] tokens of sequence b read through
+ * block_tables[b] and kv head h / (Hq / Hkv).
+ *   out           [B, Hq, D]    dtype of query; dim stride 1
+ *   query         [B, Hq, D]    f32 | f16 | bf16; dim stride 1
+ *   key_cache,
+ *   value_cache   [N, bs, Hkv, D] contiguous; dtype of query, or PA_FP8_E4M3
+ *                               with per-tensor `scale` (f16 / bf16 query)
+ *   block_tables  [B, max_blocks] i32, column stride 1, entries past
+ *                               ceil(seq_lens[b] / bs) are never read
+ *   seq_lens      [B]           i32, 0 <= seq_lens[b] <= max_blocks * bs;
+ *                               a zero length gives a zero output row
+ *   scale         score scale (1/sqrt(D) for standard attention)
+ *   block_size    bs, a multiple of 16 (16 and 32 are the usual sizes)
+ *   num_kv_heads  Hkv; Hq % Hkv must be 0
+ *   launch        stream, workspace and partitioning; NULL = null stream,
+ *                 automatic partitioning, no workspace
+ * Supported head_dim: 64, 128.  When the chosen plan splits sequences into
+ * partitions, per-partition (max, sum, partial output) triples go to the
+ * workspace and a second kernel merges them; pa_decode_workspace_bytes
+ * gives the size.  Results are deterministic (no atomics).
+ */
+int pa_decode(pa_tensor* out, const pa_tensor* query,
+              const pa_tensor* key_cache, const pa_tensor* value_cache,
+              const pa_tensor* block_tables, const pa_tensor* seq_lens,
+              float scale, int32_t block_size, int32_t num_kv_heads,
+              const pa_launch* launch);
+
+/*
+ * pa_copy_blocks -- device copy of whole physical blocks, the data step of
+ * copy-on-write ("5.KV Cache 管理 & PagedAttention", question 18,
+ * copy_block): for each row (src, dst) of block_pairs,
+ * key_cache[dst] = key_cache[src] and value_cache[dst] = value_cache[src].
+ *   key_cache, value_cache  [N, bs, Hkv, D] contiguous, any one dtype
+ *   block_pairs             [n, 2] i32 (device), rows independent; a dst
+ *                           must not appear as another row's src or dst
+ */
+int pa_copy_blocks(pa_tensor* key_cache, pa_tensor* value_cache,
+                   const pa_tensor* block_pairs, const pa_launch* launch);
+
+/*
+ * Workspace bytes pa_decode needs for these sizes and this partition request
+ * (the same plan pa_decode makes; 0 when it does not split).  max_blocks is
+ * the block-table width.  Returns a negative status on invalid sizes.
+ */
+int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t max_blocks,
+                                  int32_t partition_tokens);
+
+/*
+ * Partition size pa_decode would use (tokens; 0 = no split) for these sizes.
+ */
+int32_t pa_decode_plan_partition(int32_t batch, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks,
+                                 int32_t partition_tokens);
+
+/* Thread-local message for the last failing call on this thread. */
+const char* pa_last_error(void);
+
+/* Short build description (target, variants). */
+const char* pa_build_info(void);
+
+/* ------------------------------------------------------------------------ *
+ * Host-side block allocator ("5.KV Cache 管理 & PagedAttention", question 9).
+ * A stack of free physical block ids guarded by a mutex.  Allocation pops the
+ * top of the stack and sets the block's reference count to 1; incref shares
+ * a block; decref releases one reference and pushes the block back when the
+ * count reaches 0.  Plain CPU code: no device calls.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_allocator pa_allocator;
+
+/* free_order: the initial stack, bottom first (a permutation of 0..N-1), or
+ * NULL for 0..N-1 (the first allocation then returns N-1).  Returns NULL on
+ * invalid arguments (see pa_last_error). */
+pa_allocator* pa_alloc_create(int32_t num_blocks, const int32_t* free_order);
+void pa_alloc_destroy(pa_allocator* a);
+/* PA_ERR_OUT_OF_BLOCKS when the stack is empty. */
+int pa_alloc_allocate(pa_allocator* a, int32_t* block_out);
+/* PA_ERR_BAD_BLOCK when the id is out of range or not allocated. */
+int pa_alloc_incref(pa_allocator* a, int32_t block);
+int pa_alloc_decref(pa_allocator* a, int32_t block);
+int32_t pa_alloc_num_free(const pa_allocator* a);
+int32_t pa_alloc_num_blocks(const pa_allocator* a);
+/* reference count, or PA_ERR_BAD_BLOCK for an id out of range */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);
+
+/* ------------------------------------------------------------------------ *
+ * Sequence block manager on top of an allocator (same page, questions 10,
+ * 12, 18, 20).  Each sequence owns a block table and a length.  Appending a
+ * token allocates a block when the length fills the table and returns the
+ * token's slot; appending into a block shared with another sequence first
+ * moves the sequence to a private copy (copy-on-write) and reports the
+ * (source, destination) pair the caller must copy on the device with
+ * pa_copy_blocks before writing.  The manager does not own the allocator.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_block_manager pa_block_manager;
+
+pa_block_manager* pa_bm_create(pa_allocator* a, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* m);
+/* New sequence whose first shared_tokens tokens live in the already allocated
+ * blocks shared_blocks[0..n_shared) (each gets one more reference). */
+int pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id,
+                       const int32_t* shared_blocks, int32_t n_shared,
+                       int64_t shared_tokens);
+/* Reserve the slot of the sequence's next token; cow_src / cow_dst are -1 or
+ * the block pair to copy first.  On PA_ERR_OUT_OF_BLOCKS nothing changes. */
+int pa_bm_append_slot(pa_block_manager* m, int64_t seq_id, int64_t* slot_out,
+                      int32_t* cow_src, int32_t* cow_dst);
+/* child shares every block of parent (one more reference each). */
+int pa_bm_fork(pa_block_manager* m, int64_t parent_id, int64_t child_id);
+int pa_bm_free_sequence(pa_block_manager* m, int64_t seq_id);
+int64_t pa_bm_seq_len(const pa_block_manager* m, int64_t seq_id);
+int32_t pa_bm_num_blocks_of(const pa_block_manager* m, int64_t seq_id);
+/* Fill host arrays block_tables[n, max_blocks] (padded with -1) and
+ * seq_lens[n] for the listed sequences; PA_ERR_INVALID_ARG if a table does
+ * not fit in max_blocks. */
+int pa_bm_export(const pa_block_manager* m, const int64_t* seq_ids, int32_t n,
+                 int32_t max_blocks, int32_t* block_tables, int32_t* seq_lens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -202,3 +202,43 @@ def partitioned_decode_one(q, Kb, Vb, scale, bounds: Sequence[int]):
     if not triples:
         return np.zeros(q.shape[0])
     return merge_triples(triples)
+
+
+def paged_decode_stored(query, key_cache, value_cache, kind: str,
+                        k_scale: float, v_scale: float, block_tables: np.ndarray,
+                        seq_lens: np.ndarray, scale: float, block_size: int,
+                        pairs: Optional[Sequence] = None) -> np.ndarray:
+    """O1 on caches kept in their storage format (CPU torch tensors; fp8 as
+    uint8 codes).  Each sequence's tokens are gathered in storage format and
+    decoded exactly to fp64 (fp8: code value times the per-tensor scale)
+    before the plain definition is applied.  `pairs` limits the work to some
+    (b, h); the other rows stay NaN."""
+    import torch
+
+    from .cache_write import to_f64
+
+    q = query.to(torch.float64).numpy()
+    B, Hq, D = q.shape
+    Hkv = key_cache.shape[2]
+    if Hq % Hkv:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    g = Hq // Hkv
+    out = np.full((B, Hq, D), np.nan)
+    by_b = {}
+    for b, h in (pairs if pairs is not None else [(b, h) for b in range(B) for h in range(Hq)]):
+        by_b.setdefault(int(b), []).append(int(h))
+    for b, hs in by_b.items():
+        L = int(seq_lens[b])
+        if L == 0:
+            out[b, hs] = 0.0
+            continue
+        phys, off = token_address(block_tables[b], np.arange(L), block_size)
+        if phys.min() < 0 or phys.max() >= key_cache.shape[0]:
+            raise IndexError("block table entry outside the physical pool")
+        pi, oi = torch.from_numpy(phys), torch.from_numpy(off)
+        Kb = to_f64(key_cache[pi, oi], kind, k_scale)          # [L, Hkv, D]
+        Vb = to_f64(value_cache[pi, oi], kind, v_scale)
+        for h in hs:
+            kvh = kv_head_for(h, g)
+            out[b, h] = softmax_attend(q[b, h], Kb[:, kvh, :], Vb[:, kvh, :], scale)
+    return out

@@ -1,0 +1,22 @@
+"""MI355X (gfx950) paged decode attention.
+
+The compute lives in libpa.so (hand-written HIP kernels behind a C ABI,
+declared in include/pa.h).  This package is a thin binding: it marshals torch
+tensors into the library's plain descriptors and calls it.  There is no
+fallback: if libpa.so is missing, every call raises.
+"""
+
+from ._lib import LibraryMissing, PaError, lib_path, load  # noqa: F401
+from .ops import (  # noqa: F401
+    PATH_AUTO,
+    PATH_MFMA,
+    PATH_VALU,
+    BlockAllocator,
+    BlockManager,
+    build_info,
+    copy_blocks,
+    decode,
+    decode_plan_partition,
+    decode_workspace_bytes,
+    reshape_and_cache,
+)

@@ -1,0 +1,352 @@
+// C-ABI entry points: host-side validation, planning and dispatch.
+//
+// Every check below runs before any HIP call, so an invalid request returns
+// an error code without touching the device (and can be tested on a machine
+// without a GPU).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int elem_size(int dt) {
+  switch (dt) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    case PA_FP8_E4M3: return 1;
+    case PA_I32: return 4;
+    case PA_I64: return 8;
+    default: return 0;
+  }
+}
+
+int kind_of(int dt) {
+  switch (dt) {
+    case PA_F32: return pa::K_F32;
+    case PA_F16: return pa::K_F16;
+    case PA_BF16: return pa::K_BF16;
+    case PA_FP8_E4M3: return pa::K_FP8;
+    default: return -1;
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_tensor(const pa_tensor* t, const char* name, int ndim) {
+  if (!t) return fail(PA_ERR_INVALID_ARG, "%s: null descriptor", name);
+  if (t->ndim != ndim) return fail(PA_ERR_INVALID_ARG, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  if (elem_size(t->dtype) == 0) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, t->dtype);
+  int64_t numel = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative extent", name);
+    numel *= t->shape[i];
+  }
+  if (numel > 0 && !t->data) return fail(PA_ERR_INVALID_ARG, "%s: null data", name);
+  return PA_OK;
+}
+
+bool contiguous(const pa_tensor* t) {
+  int64_t s = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != s) return false;
+    s *= t->shape[i];
+  }
+  return true;
+}
+
+int check_cache_pair(const pa_tensor* k, const pa_tensor* v) {
+  int rc;
+  if ((rc = check_tensor(k, "key_cache", 4)) || (rc = check_tensor(v, "value_cache", 4))) return rc;
+  for (int i = 0; i < 4; ++i)
+    if (k->shape[i] != v->shape[i]) return fail(PA_ERR_INVALID_ARG, "key_cache and value_cache shapes differ");
+  if (k->dtype != v->dtype) return fail(PA_ERR_INVALID_ARG, "key_cache and value_cache dtypes differ");
+  if (!contiguous(k) || !contiguous(v))
+    return fail(PA_ERR_INVALID_ARG, "caches must be contiguous [num_blocks, block_size, num_kv_heads, head_dim]");
+  if (kind_of(k->dtype) < 0) return fail(PA_ERR_INVALID_ARG, "cache dtype must be f32, f16, bf16 or fp8");
+  if (!aligned16(k->data) || !aligned16(v->data)) return fail(PA_ERR_INVALID_ARG, "caches must be 16-byte aligned");
+  if (k->dtype == PA_FP8_E4M3) {
+    if (!(k->scale > 0.f) || !isfinite(k->scale) || !(v->scale > 0.f) || !isfinite(v->scale))
+      return fail(PA_ERR_INVALID_ARG, "fp8 caches need a positive finite scale");
+  }
+  return PA_OK;
+}
+
+struct Plan {
+  int split = 0;
+  int part_tokens = 0;
+  int num_parts = 1;
+  int64_t ws_bytes = 0;
+};
+
+// Shared by pa_decode and the workspace query.  The host never reads
+// seq_lens (they live on the device), so the grid covers the table width;
+// partitions past a sequence's end exit at once.
+int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
+  if (Hq % Hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", Hq, Hkv);
+  if (bs % 16) return fail(PA_ERR_UNSUPPORTED, "block_size must be a multiple of 16 (got %d)", bs);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+  const int64_t max_ctx64 = (int64_t)max_blocks * bs;
+  if (max_ctx64 > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "block table addresses too many tokens");
+  const int max_ctx = (int)max_ctx64;
+  Plan p;
+  int pt = req;
+  if (pt == 0) pt = 512;  // automatic: 512-token partitions for long contexts
+  if (pt > 0 && pt % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of 16");
+  if (pt < -1) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be -1, 0 or positive");
+  if (pt == -1 || pt >= max_ctx) {
+    p.split = 0;
+    p.part_tokens = max_ctx > 0 ? ((max_ctx + 15) / 16) * 16 : 16;
+    p.num_parts = 1;
+  } else {
+    p.split = 1;
+    p.part_tokens = pt;
+    p.num_parts = (max_ctx + pt - 1) / pt;
+    if (p.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", p.num_parts);
+    p.ws_bytes = (int64_t)B * Hq * p.num_parts * (D + 2) * (int64_t)sizeof(float);
+  }
+  *out = p;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+const char* pa_build_info(void) {
+  return "target gfx950 (CDNA4); decode VALU {f32,f16,bf16,fp8-kv} x head_dim {64,128} x "
+         "heads/tile {1,2,4}; decode MFMA {f16,bf16,fp8-kv} x head_dim {64,128} x 16 heads/tile; "
+         "split-partition merge; cache write {copy, fp8 e4m3 quantise}; block copy";
+}
+
+int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                                  int32_t partition_tokens) {
+  Plan p;
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
+                     partition_tokens, &p);
+  return rc ? rc : p.ws_bytes;
+}
+
+int32_t pa_decode_plan_partition(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                                 int32_t partition_tokens) {
+  Plan p;
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
+                     partition_tokens, &p);
+  return rc ? rc : (p.split ? p.part_tokens : 0);
+}
+
+int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+              const pa_tensor* value_cache, const pa_tensor* block_tables,
+              const pa_tensor* seq_lens, float scale, int32_t block_size,
+              int32_t num_kv_heads, const pa_launch* launch) {
+  int rc;
+  if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(out, "out", 3)) ||
+      (rc = check_cache_pair(key_cache, value_cache)) ||
+      (rc = check_tensor(block_tables, "block_tables", 2)) ||
+      (rc = check_tensor(seq_lens, "seq_lens", 1)))
+    return rc;
+  const int qdt = query->dtype;
+  if (qdt != PA_F32 && qdt != PA_F16 && qdt != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "query dtype must be f32, f16 or bf16");
+  if (out->dtype != qdt) return fail(PA_ERR_INVALID_ARG, "out dtype must equal the query dtype");
+  const int64_t B = query->shape[0], Hq = query->shape[1], D = query->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != query->shape[i]) return fail(PA_ERR_INVALID_ARG, "out shape must equal the query shape");
+  if (query->stride[2] != 1 || out->stride[2] != 1)
+    return fail(PA_ERR_INVALID_ARG, "query/out head_dim stride must be 1");
+  const int64_t N = key_cache->shape[0], bs = key_cache->shape[1], Hkv = key_cache->shape[2];
+  if (key_cache->shape[3] != D) return fail(PA_ERR_INVALID_ARG, "cache head_dim %lld != query head_dim %lld",
+                                            (long long)key_cache->shape[3], (long long)D);
+  if (bs != block_size) return fail(PA_ERR_INVALID_ARG, "block_size %d != cache block dimension %lld",
+                                    block_size, (long long)bs);
+  if (Hkv != num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d != cache head dimension %lld",
+                                       num_kv_heads, (long long)Hkv);
+  const int kvdt = key_cache->dtype;
+  if (!(kvdt == qdt || (kvdt == PA_FP8_E4M3 && (qdt == PA_F16 || qdt == PA_BF16))))
+    return fail(PA_ERR_INVALID_ARG, "cache dtype must equal the query dtype, or be fp8 with an f16/bf16 query");
+  if (block_tables->dtype != PA_I32 || seq_lens->dtype != PA_I32)
+    return fail(PA_ERR_INVALID_ARG, "block_tables and seq_lens must be int32");
+  if (block_tables->shape[0] != B || seq_lens->shape[0] != B)
+    return fail(PA_ERR_INVALID_ARG, "block_tables / seq_lens batch must equal the query batch");
+  if (block_tables->stride[1] != 1 || (seq_lens->stride[0] != 1 && B > 1))
+    return fail(PA_ERR_INVALID_ARG, "block_tables column stride and seq_lens stride must be 1");
+  const int64_t max_blocks = block_tables->shape[1];
+  if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "batch above 65535");
+  if (N > 0x7FFFFFFFLL || max_blocks > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "pool or table too large");
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  const int qes = elem_size(qdt);
+  const int64_t vec = 16 / qes;
+  if (!aligned16(query->data) || query->stride[0] % vec || query->stride[1] % vec)
+    return fail(PA_ERR_INVALID_ARG, "query rows must be 16-byte aligned");
+  Plan plan;
+  if ((rc = make_plan((int)B, (int)Hq, (int)Hkv, (int)D, (int)bs, (int)max_blocks,
+                      launch ? launch->partition_tokens : 0, &plan)))
+    return rc;
+  const int G = (int)(Hq / Hkv);
+  const int req_path = launch ? launch->path : PA_PATH_AUTO;
+  pa::DecodeVariant v;
+  v.qkind = kind_of(qdt);
+  v.kvkind = kind_of(kvdt);
+  v.D = (int)D;
+  if (req_path == PA_PATH_MFMA) {
+    if (qdt == PA_F32) return fail(PA_ERR_UNSUPPORTED, "the MFMA path needs an f16/bf16 query");
+    v.path = 2;
+  } else if (req_path == PA_PATH_VALU) {
+    v.path = 1;
+  } else if (req_path == PA_PATH_AUTO) {
+    v.path = (qdt != PA_F32 && G >= 4) ? 2 : 1;
+  } else {
+    return fail(PA_ERR_INVALID_ARG, "unknown path %d", req_path);
+  }
+  v.gt = v.path == 2 ? 16 : (G == 1 ? 1 : (G == 2 ? 2 : 4));
+  if (!pa::decode_variant_built(v)) return fail(PA_ERR_UNSUPPORTED, "no decode variant for this dtype / head_dim");
+  if (plan.split) {
+    if (!launch || !launch->workspace || launch->workspace_bytes < (size_t)plan.ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "split decode needs %lld workspace bytes", (long long)plan.ws_bytes);
+  }
+  if (B == 0 || Hq == 0) return PA_OK;
+
+  pa::DecodeParams p;
+  memset(&p, 0, sizeof p);
+  p.out = out->data;
+  p.q = query->data;
+  p.kc = key_cache->data;
+  p.vc = value_cache->data;
+  p.tables = static_cast<const int32_t*>(block_tables->data);
+  p.lens = static_cast<const int32_t*>(seq_lens->data);
+  p.q_sb = query->stride[0];
+  p.q_sh = query->stride[1];
+  p.o_sb = out->stride[0];
+  p.o_sh = out->stride[1];
+  p.tab_stride = block_tables->stride[0];
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.G = G;
+  p.D = (int)D;
+  p.bs = (int)bs;
+  p.max_blocks = (int)max_blocks;
+  p.num_blocks = (int)N;
+  p.head_tiles = (G + v.gt - 1) / v.gt;
+  p.part_tokens = plan.part_tokens;
+  p.num_parts = plan.num_parts;
+  p.split = plan.split;
+  const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
+  p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
+  p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
+  if (plan.split) {
+    p.ws_acc = static_cast<float*>(launch->workspace);
+    p.ws_ml = p.ws_acc + (int64_t)B * Hq * plan.num_parts * D;
+  }
+  if ((int64_t)Hkv * p.head_tiles > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  hipError_t e = pa::launch_decode(p, v, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value, const pa_tensor* slot_mapping,
+                         pa_tensor* key_cache, pa_tensor* value_cache, const pa_launch* launch) {
+  int rc;
+  if ((rc = check_tensor(key, "key", 3)) || (rc = check_tensor(value, "value", 3)) ||
+      (rc = check_tensor(slot_mapping, "slot_mapping", 1)) ||
+      (rc = check_cache_pair(key_cache, value_cache)))
+    return rc;
+  const int sdt = key->dtype;
+  if (value->dtype != sdt) return fail(PA_ERR_INVALID_ARG, "key and value dtypes differ");
+  if (sdt != PA_F32 && sdt != PA_F16 && sdt != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "key/value dtype must be f32, f16 or bf16");
+  const int cdt = key_cache->dtype;
+  if (cdt != sdt && cdt != PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "cache dtype must equal the key dtype or be fp8");
+  const int64_t T = key->shape[0], Hkv = key->shape[1], D = key->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (value->shape[i] != key->shape[i]) return fail(PA_ERR_INVALID_ARG, "key and value shapes differ");
+  if (slot_mapping->dtype != PA_I64 || slot_mapping->shape[0] != T)
+    return fail(PA_ERR_INVALID_ARG, "slot_mapping must be int64 [num_tokens]");
+  if (T > 1 && slot_mapping->stride[0] != 1) return fail(PA_ERR_INVALID_ARG, "slot_mapping must be contiguous");
+  if (key_cache->shape[2] != Hkv || key_cache->shape[3] != D)
+    return fail(PA_ERR_INVALID_ARG, "cache [.., .., Hkv, D] must match key [T, Hkv, D]");
+  if (key->stride[2] != 1 || value->stride[2] != 1 || key->stride[1] != D || value->stride[1] != D)
+    return fail(PA_ERR_INVALID_ARG, "key/value rows [Hkv, D] must be contiguous");
+  if ((Hkv * D) % 8) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads * head_dim must be a multiple of 8");
+  const int64_t vec = 16 / elem_size(sdt);
+  if (!aligned16(key->data) || !aligned16(value->data) || (T > 1 && (key->stride[0] % vec || value->stride[0] % vec)))
+    return fail(PA_ERR_INVALID_ARG, "key/value token rows must be 16-byte aligned");
+  if (T == 0) return PA_OK;
+  pa::CacheWriteParams p;
+  memset(&p, 0, sizeof p);
+  p.key = key->data;
+  p.value = value->data;
+  p.slots = static_cast<const int64_t*>(slot_mapping->data);
+  p.kc = key_cache->data;
+  p.vc = value_cache->data;
+  p.k_stride_tok = key->stride[0];
+  p.v_stride_tok = value->stride[0];
+  p.T = T;
+  p.Hkv = (int)Hkv;
+  p.D = (int)D;
+  p.bs = (int)key_cache->shape[1];
+  p.num_slots = key_cache->shape[0] * key_cache->shape[1];
+  p.k_scale = key_cache->scale;
+  p.v_scale = value_cache->scale;
+  hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  hipError_t e = pa::launch_cache_write(p, kind_of(sdt), kind_of(cdt), stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_copy_blocks(pa_tensor* key_cache, pa_tensor* value_cache, const pa_tensor* block_pairs,
+                   const pa_launch* launch) {
+  int rc;
+  if ((rc = check_cache_pair(key_cache, value_cache)) || (rc = check_tensor(block_pairs, "block_pairs", 2)))
+    return rc;
+  if (block_pairs->dtype != PA_I32 || block_pairs->shape[1] != 2 || !contiguous(block_pairs))
+    return fail(PA_ERR_INVALID_ARG, "block_pairs must be contiguous int32 [n, 2]");
+  const int64_t bytes = key_cache->shape[1] * key_cache->shape[2] * key_cache->shape[3] *
+                        elem_size(key_cache->dtype);
+  if (bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+  pa::CopyBlocksParams p;
+  p.kc = key_cache->data;
+  p.vc = value_cache->data;
+  p.pairs = static_cast<const int32_t*>(block_pairs->data);
+  p.n = block_pairs->shape[0];
+  p.block_bytes = bytes;
+  p.num_blocks = key_cache->shape[0];
+  if (p.n == 0) return PA_OK;
+  hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  hipError_t e = pa::launch_copy_blocks(p, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "block copy launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // extern "C"
+
+// shared with the allocator translation unit
+namespace pa {
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace pa

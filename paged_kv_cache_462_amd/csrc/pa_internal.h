@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI layer (pa_api.cpp) and the HIP
+// launchers.  Host code only; no torch types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Kind : int { K_F32 = 0, K_F16 = 1, K_BF16 = 2, K_FP8 = 3 };
+
+// Everything the decode kernels read, resolved on the host.
+struct DecodeParams {
+  void* out;              // [B, Hq, D] query dtype
+  const void* q;          // [B, Hq, D]
+  const void* kc;         // [N, bs, Hkv, D]
+  const void* vc;
+  const int32_t* tables;  // [B, tab_stride]
+  const int32_t* lens;    // [B]
+  float* ws_acc;          // [B, Hq, P, D] partial outputs (split only)
+  float* ws_ml;           // [B, Hq, P, 2] (max, sum) (split only)
+  int64_t q_sb, q_sh;     // query strides (elements)
+  int64_t o_sb, o_sh;     // output strides
+  int64_t tab_stride;     // block-table row stride
+  int32_t B, Hq, Hkv, G, D, bs, max_blocks;
+  int32_t num_blocks;     // physical pool size
+  int32_t head_tiles;     // ceil(G / tile heads)
+  int32_t part_tokens;    // tokens per partition (multiple of 16)
+  int32_t num_parts;      // partitions per sequence in the grid (>= 1)
+  int32_t split;          // 1: write triples and merge afterwards
+  float qk_scale_log2;    // scale * k_scale * log2(e)
+  float v_scale;          // fp8 V scale (1 otherwise)
+};
+
+struct DecodeVariant {
+  int qkind;   // K_F32 / K_F16 / K_BF16
+  int kvkind;  // K_F32 / K_F16 / K_BF16 / K_FP8
+  int D;
+  int path;    // 1 VALU, 2 MFMA
+  int gt;      // query heads per workgroup tile (MFMA: 16; VALU: 1, 2 or 4)
+};
+
+// Launch the decode (and the merge when p.split).  Returns hipSuccess or the
+// launch error; hipErrorNotSupported when no variant matches.
+hipError_t launch_decode(const DecodeParams& p, const DecodeVariant& v,
+                         hipStream_t stream);
+
+struct CacheWriteParams {
+  const void* key;        // [T, Hkv, D]
+  const void* value;
+  const int64_t* slots;   // [T]
+  void* kc;               // [N, bs, Hkv, D]
+  void* vc;
+  int64_t k_stride_tok, v_stride_tok;  // elements between tokens of key/value
+  int64_t T;
+  int32_t Hkv, D, bs;
+  int64_t num_slots;      // N * bs (slots beyond are ignored)
+  float k_scale, v_scale; // fp8 caches
+};
+
+hipError_t launch_cache_write(const CacheWriteParams& p, int src_kind,
+                              int cache_kind, hipStream_t stream);
+
+struct CopyBlocksParams {
+  void* kc;
+  void* vc;
+  const int32_t* pairs;   // [n, 2]
+  int64_t n;
+  int64_t block_bytes;    // bytes of one physical block (bs * Hkv * D * esize)
+  int64_t num_blocks;
+};
+
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
+
+// Variants built into this library (for pa_build_info / validation).
+bool decode_variant_built(const DecodeVariant& v);
+
+}  // namespace pa

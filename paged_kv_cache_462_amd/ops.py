@@ -1,0 +1,229 @@
+"""Python entry points with the C ABI's names (include/pa.h).
+
+Argument marshalling only: torch tensors become `pa_tensor` descriptors,
+torch's current stream becomes the launch stream, and every step of the
+computation runs in libpa.so.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import byref, c_int32, c_int64
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import PaLaunch, PaTensor, check, load
+
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+
+_CODES = {
+    torch.float32: _lib.PA_F32,
+    torch.float16: _lib.PA_F16,
+    torch.bfloat16: _lib.PA_BF16,
+    torch.float8_e4m3fn: _lib.PA_FP8_E4M3,
+    torch.int32: _lib.PA_I32,
+    torch.int64: _lib.PA_I64,
+}
+
+
+def _desc(t: torch.Tensor, fp8: bool = False, scale: float = 1.0) -> PaTensor:
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = PaTensor()
+    d.data = t.data_ptr() if t.numel() else None
+    if fp8 or t.dtype == torch.float8_e4m3fn:
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError("an fp8 tensor must be uint8 or float8_e4m3fn")
+        d.dtype = _lib.PA_FP8_E4M3
+    else:
+        if t.dtype not in _CODES:
+            raise TypeError(f"unsupported dtype {t.dtype}")
+        d.dtype = _CODES[t.dtype]
+    d.ndim = t.dim()
+    for i, (s, st) in enumerate(zip(t.shape, t.stride())):
+        d.shape[i] = s
+        d.stride[i] = st
+    d.scale = float(scale)
+    return d
+
+
+def _launch(ref: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+            partition_tokens: int = 0, path: int = PATH_AUTO,
+            stream: Optional[torch.cuda.Stream] = None) -> PaLaunch:
+    ln = PaLaunch()
+    if ref.is_cuda:
+        s = stream if stream is not None else torch.cuda.current_stream(ref.device)
+        ln.stream = s.cuda_stream
+    else:
+        ln.stream = None
+    if workspace is not None:
+        ln.workspace = workspace.data_ptr()
+        ln.workspace_bytes = workspace.numel() * workspace.element_size()
+    ln.partition_tokens = int(partition_tokens)
+    ln.path = int(path)
+    return ln
+
+
+def _is_fp8(t: torch.Tensor, kv_dtype: Optional[str]) -> bool:
+    return kv_dtype == "fp8" or t.dtype == torch.float8_e4m3fn
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+                      key_cache: torch.Tensor, value_cache: torch.Tensor,
+                      k_scale: float = 1.0, v_scale: float = 1.0,
+                      kv_dtype: Optional[str] = None,
+                      stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_reshape_and_cache: key/value [T, Hkv, D] into slots of the caches."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    args = (_desc(key), _desc(value), _desc(slot_mapping),
+            _desc(key_cache, fp8, k_scale), _desc(value_cache, fp8, v_scale))
+    ln = _launch(key_cache, stream=stream)
+    check(load().pa_reshape_and_cache(*(byref(a) for a in args), byref(ln)))
+
+
+def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           block_size: int, max_blocks: int, partition_tokens: int = 0) -> int:
+    return check(load().pa_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                  block_size, max_blocks, partition_tokens))
+
+
+def decode_plan_partition(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          block_size: int, max_blocks: int, partition_tokens: int = 0) -> int:
+    return check(load().pa_decode_plan_partition(batch, num_q_heads, num_kv_heads, head_dim,
+                                                 block_size, max_blocks, partition_tokens))
+
+
+def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+           value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+           scale: float, block_size: int, num_kv_heads: int,
+           k_scale: float = 1.0, v_scale: float = 1.0, kv_dtype: Optional[str] = None,
+           workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+           path: int = PATH_AUTO, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_decode.  When the plan splits and no workspace is given, one is
+    allocated here (torch owns it); pass `workspace` to avoid that."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    if workspace is None:
+        need = decode_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
+                                      query.shape[2], block_size, block_tables.shape[1],
+                                      partition_tokens)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+    args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
+            _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens))
+    ln = _launch(query, workspace, partition_tokens, path, stream)
+    check(load().pa_decode(*(byref(a) for a in args), ctypes.c_float(scale),
+                           int(block_size), int(num_kv_heads), byref(ln)))
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,
+                kv_dtype: Optional[str] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_copy_blocks: key/value_cache[dst] = key/value_cache[src] per pair."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    args = (_desc(key_cache, fp8, 1.0), _desc(value_cache, fp8, 1.0), _desc(block_pairs))
+    ln = _launch(key_cache, stream=stream)
+    check(load().pa_copy_blocks(*(byref(a) for a in args), byref(ln)))
+
+
+def build_info() -> str:
+    return load().pa_build_info().decode()
+
+
+class BlockAllocator:
+    """pa_alloc_*: ref-counted LIFO block allocator (host)."""
+
+    def __init__(self, num_blocks: int, free_order: Optional[Sequence[int]] = None):
+        lib = load()
+        arr = None
+        if free_order is not None:
+            fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            arr = fo.ctypes.data_as(ctypes.POINTER(c_int32))
+        h = lib.pa_alloc_create(int(num_blocks), arr)
+        if not h:
+            raise _lib.PaError(_lib.PA_ERR_INVALID_ARG, _lib.last_error())
+        self._h = h
+        self._lib = lib
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_alloc_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def allocate(self) -> int:
+        out = c_int32()
+        check(self._lib.pa_alloc_allocate(self._h, byref(out)))
+        return out.value
+
+    def incref(self, block: int) -> None:
+        check(self._lib.pa_alloc_incref(self._h, int(block)))
+
+    def decref(self, block: int) -> None:
+        check(self._lib.pa_alloc_decref(self._h, int(block)))
+
+    def num_free(self) -> int:
+        return check(self._lib.pa_alloc_num_free(self._h))
+
+    def num_blocks(self) -> int:
+        return check(self._lib.pa_alloc_num_blocks(self._h))
+
+    def refcount(self, block: int) -> int:
+        return check(self._lib.pa_alloc_refcount(self._h, int(block)))
+
+
+class BlockManager:
+    """pa_bm_*: per-sequence block tables over a BlockAllocator (host)."""
+
+    def __init__(self, allocator: BlockAllocator, block_size: int):
+        self._lib = load()
+        self._alloc = allocator  # keep alive
+        h = self._lib.pa_bm_create(allocator.handle, int(block_size))
+        if not h:
+            raise _lib.PaError(_lib.PA_ERR_INVALID_ARG, _lib.last_error())
+        self._h = h
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_bm_destroy(h)
+            self._h = None
+
+    def add_sequence(self, seq_id: int, shared_blocks: Sequence[int] = (),
+                     shared_tokens: int = 0) -> None:
+        arr = np.ascontiguousarray(np.asarray(list(shared_blocks), dtype=np.int32))
+        ptr = arr.ctypes.data_as(ctypes.POINTER(c_int32)) if len(arr) else None
+        check(self._lib.pa_bm_add_sequence(self._h, int(seq_id), ptr, len(arr), int(shared_tokens)))
+
+    def append_slot(self, seq_id: int):
+        slot, src, dst = c_int64(), c_int32(), c_int32()
+        check(self._lib.pa_bm_append_slot(self._h, int(seq_id), byref(slot), byref(src), byref(dst)))
+        return slot.value, src.value, dst.value
+
+    def fork(self, parent: int, child: int) -> None:
+        check(self._lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free_sequence(self, seq_id: int) -> None:
+        check(self._lib.pa_bm_free_sequence(self._h, int(seq_id)))
+
+    def seq_len(self, seq_id: int) -> int:
+        return check(self._lib.pa_bm_seq_len(self._h, int(seq_id)))
+
+    def num_blocks_of(self, seq_id: int) -> int:
+        return check(self._lib.pa_bm_num_blocks_of(self._h, int(seq_id)))
+
+    def export(self, seq_ids: Sequence[int], max_blocks: int):
+        ids = np.ascontiguousarray(np.asarray(list(seq_ids), dtype=np.int64))
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        check(self._lib.pa_bm_export(self._h, ids.ctypes.data_as(ctypes.POINTER(c_int64)),
+                                     len(ids), int(max_blocks),
+                                     tables.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                     lens.ctypes.data_as(ctypes.POINTER(c_int32))))
+        return tables, lens
