@@ -7,6 +7,11 @@ attention of every query head over its sequence's paged K/V
 (pa_decode: partition kernel, plus the merge kernel when the plan splits).
 Inputs are synthetic and seeded (synth/), resident in HBM before timing.
 
+Like the layers of a model, consecutive steps use different copies of the
+KV pool (enough copies that together they are several times the 256 MB
+last-level cache), so no step reads K/V that an earlier step left in cache.
+A back-to-back run on a single copy is reported beside it for context.
+
 Prints ONE JSON line:
   value           KV GB/s over the whole timed step (algorithmic KV bytes of
                   the batch / step time)
@@ -112,7 +117,9 @@ def main() -> int:
     ap.add_argument("--config", default="c2", help="workload name or c1..c5 (default: the 7B-shaped decode)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
-    ap.add_argument("--flushed-iters", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
+    ap.add_argument("--hot-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -152,6 +159,15 @@ def main() -> int:
     pa.reshape_and_cache(wl.tok_key.to(dev), wl.tok_value.to(dev),
                          torch.from_numpy(wl.slot_mapping).to(dev), kc, vc,
                          k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
+    pool_bytes = 2 * kc.numel() * kc.element_size()
+    n_layers = args.layers or max(1, -(-(3 << 30) // pool_bytes))
+    layers = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n_layers - 1)]
+    # a plain copy of known size (256 MiB read + 256 MiB written): the
+    # calibration kernel for the FETCH_SIZE / WRITE_SIZE counters
+    cal_src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
     new_k = wl.new_key().to(dev)
     new_v = wl.new_value().to(dev)
     new_slots = torch.from_numpy(wl.new_slots).to(dev)
@@ -164,19 +180,21 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    def decode():
-        pa.decode(out, q, kc, vc, tables, lens, wl.scale, c.block_size, c.num_kv_heads,
+    def decode(layer):
+        k_, v_ = layers[layer]
+        pa.decode(out, q, k_, v_, tables, lens, wl.scale, c.block_size, c.num_kv_heads,
                   k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, workspace=ws,
                   partition_tokens=args.partition_tokens, path=args.path)
 
-    def step():
-        pa.reshape_and_cache(new_k, new_v, new_slots, kc, vc, k_scale=wl.k_scale,
+    def write(layer):
+        k_, v_ = layers[layer]
+        pa.reshape_and_cache(new_k, new_v, new_slots, k_, v_, k_scale=wl.k_scale,
                              v_scale=wl.v_scale, kv_dtype=kvd)
-        decode()
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    log(f"[bench] {n_layers} KV pool copies of {pool_bytes / 1e6:.0f} MB; warmup {args.warmup}")
+    for i in range(args.warmup):
+        write(i % n_layers)
+        decode(i % n_layers)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -185,10 +203,9 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        pa.reshape_and_cache(new_k, new_v, new_slots, kc, vc, k_scale=wl.k_scale,
-                             v_scale=wl.v_scale, kv_dtype=kvd)
+        write(i % n_layers)
         evs[i][0].record(stream)
-        decode()
+        decode(i % n_layers)
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -197,19 +214,16 @@ def main() -> int:
     dec_mean = float(np.mean(dec_ms))
     dec_med = float(np.median(dec_ms))
 
-    # decode with L2 and MALL flushed before every launch (1 GiB written)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    fl_ms = []
-    for _ in range(args.flushed_iters):
-        flush.zero_()
+    # context: the same copy decoded back to back (part of it stays in cache)
+    hot_ms = []
+    for _ in range(args.hot_iters):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        decode()
+        decode(0)
         b.record(stream)
         b.synchronize()
-        fl_ms.append(a.elapsed_time(b))
-    del flush
-    fl_med = float(np.median(fl_ms)) if fl_ms else None
+        hot_ms.append(a.elapsed_time(b))
+    hot_med = float(np.median(hot_ms)) if hot_ms else None
 
     kv_unique = wl.unique_kv_bytes()
     kv_logical = wl.logical_kv_bytes()
@@ -228,8 +242,9 @@ def main() -> int:
         "algorithmic_bytes_per_launch": kv_unique,
         "mean_launch_ms": round(dec_mean, 5),
         "median_launch_ms": round(dec_med, 5),
-        "flushed_median_launch_ms": round(fl_med, 5) if fl_med else None,
-        "flushed_GBps": round(kv_unique / (fl_med * 1e-3) / 1e9, 1) if fl_med else None,
+        "kv_pool_copies": n_layers,
+        "same_copy_back_to_back_median_ms": round(hot_med, 5) if hot_med else None,
+        "same_copy_back_to_back_GBps": round(kv_unique / (hot_med * 1e-3) / 1e9, 1) if hot_med else None,
     }
     res = {
         "metric": METRIC,
