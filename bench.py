@@ -53,16 +53,22 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str, launch_desc: str):
-    """HBM bytes per launch from the committed counter summary, if it was
+    """HBM bytes per launch from the committed counter summary
+    (profiles/pa_decode_<workload>_traffic.txt, `key: value` lines), if it was
     taken on the current decode kernel source and launch plan."""
-    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
+    t = {}
     with open(path) as f:
-        t = json.load(f)
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            t[k.strip()] = v.strip()
     if t.get("kernel_source_sha") != kernel_source_hash() or t.get("launch") != launch_desc:
         return None
-    return t
+    return {"hbm_bytes_per_launch": int(t["hbm_bytes_per_launch"])}
 
 
 def cpu_baseline(wl, seconds: float):
