@@ -116,7 +116,8 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
  * pa_decode -- out[b, h] = softmax(scale * q[b, h] . K_b^T) V_b, where K_b, V_b
  * are the first seq_lens[b] tokens of sequence b read through
  * block_tables[b] and kv head h / (Hq / Hkv).
- *   out           [B, Hq, D]    dtype of query; dim stride 1
+ *   out           [B, Hq, D]    dtype of query; dim stride 1; rows 16-byte
+ *                               aligned (like the query's)
  *   query         [B, Hq, D]    f32 | f16 | bf16; dim stride 1
  *   key_cache,
  *   value_cache   [N, bs, Hkv, D] contiguous; dtype of query, or PA_FP8_E4M3
@@ -128,8 +129,8 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
  *   scale         score scale (1/sqrt(D) for standard attention)
  *   block_size    bs, a multiple of 16 (16 and 32 are the usual sizes)
  *   num_kv_heads  Hkv; Hq % Hkv must be 0
- *   launch        stream, workspace and partitioning; NULL = null stream,
- *                 automatic partitioning, no workspace
+ *   launch        stream, workspace (16-byte aligned) and partitioning;
+ *                 NULL = null stream, automatic partitioning, no workspace
  * Supported head_dim: 64, 128.  When the chosen plan splits sequences into
  * partitions, per-partition (max, sum, partial output) triples go to the
  * workspace and a second kernel merges them; pa_decode_workspace_bytes

@@ -202,6 +202,8 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   const int64_t vec = 16 / qes;
   if (!aligned16(query->data) || query->stride[0] % vec || query->stride[1] % vec)
     return fail(PA_ERR_INVALID_ARG, "query rows must be 16-byte aligned");
+  if (!aligned16(out->data) || out->stride[0] % vec || out->stride[1] % vec)
+    return fail(PA_ERR_INVALID_ARG, "out rows must be 16-byte aligned");
   Plan plan;
   if ((rc = make_plan((int)B, (int)Hq, (int)Hkv, (int)D, (int)bs, (int)max_blocks,
                       launch ? launch->partition_tokens : 0, &plan)))
@@ -227,6 +229,7 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   if (plan.split) {
     if (!launch || !launch->workspace || launch->workspace_bytes < (size_t)plan.ws_bytes)
       return fail(PA_ERR_WORKSPACE, "split decode needs %lld workspace bytes", (long long)plan.ws_bytes);
+    if (!aligned16(launch->workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
   if (B == 0 || Hq == 0) return PA_OK;
 
@@ -252,6 +255,10 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   p.max_blocks = (int)max_blocks;
   p.num_blocks = (int)N;
   p.head_tiles = (G + v.gt - 1) / v.gt;
+  const int64_t units = Hkv * (int64_t)p.head_tiles;
+  if (units > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  p.units = (int)units;
+  p.waves = (int)(units < pa::decode_max_waves() ? units : pa::decode_max_waves());
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
@@ -262,7 +269,6 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
     p.ws_acc = static_cast<float*>(launch->workspace);
     p.ws_ml = p.ws_acc + (int64_t)B * Hq * plan.num_parts * D;
   }
-  if ((int64_t)Hkv * p.head_tiles > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_decode(p, v, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));

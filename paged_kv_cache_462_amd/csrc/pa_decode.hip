@@ -10,30 +10,43 @@
 // softmax).  Query heads share kv heads in groups of G = Hq / Hkv
 // (same page, question 7).
 //
-// Work decomposition: one workgroup (4 waves) per (sequence, kv head, head
-// tile, partition).  A partition is `part_tokens` consecutive tokens; the
-// waves of a workgroup take its 16-token tiles round-robin, each keeping its
-// own softmax state, and the states are merged through LDS.  With a split,
-// each partition leaves a (max, sum, unnormalised output) triple in the
-// workspace and merge_kernel combines them in a fixed order (no atomics, so
-// results are bit-reproducible).
+// Work decomposition.  A work unit is one (kv head, tile of query heads of
+// its group); one wave owns one unit over one partition of one sequence and
+// walks every 16-token tile of that partition itself, so its softmax state
+// never has to be merged with another wave's.  A workgroup is up to eight
+// consecutive units of the same (sequence, partition): its waves read the
+// same physical blocks at the same time, so each block's K (and V) rows of
+// neighbouring heads, which are adjacent in memory, are fetched together.
+// On MI355X that keeps the DRAM access stream close to a sequential one
+// (6.9 TB/s for the bare gather, against 5.7 TB/s when each workgroup walks
+// one head on its own).  With a split, each partition leaves a
+// (max, sum, unnormalised output) triple in the workspace and merge_kernel
+// combines them in a fixed order (no atomics, so results are
+// bit-reproducible).
+//
+// Every K/V load reads whole token rows (16 lanes x 16 bytes for a 256-byte
+// row), so a load instruction covers complete 128-byte lines.
 //
 // Two inner loops:
 //  * VALU (small groups): lanes of a row of LPT lanes cover one token's
-//    head_dim with 16-byte loads; q.k partial dot products (v_dot2 for 16-bit
-//    data) are summed across the row with DPP; every row keeps its own
-//    online-softmax state.
+//    head_dim; q.k partial dot products (v_dot2 for 16-bit data) are summed
+//    across the row with DPP; every row keeps its own online-softmax state
+//    and the rows are merged with lane shuffles at the end.
 //  * MFMA (groups >= 4): scores = K-tile[16 x D] x Q-group^T[D x 16] on
 //    v_mfma_f32_16x16x32, then out^T += V^T[D x 16] x P^T[16 x 16] on
-//    v_mfma_f32_16x16x16.  The score tile comes out with lane l holding
-//    tokens 4*(l/16)+i of head l%16, which is exactly the layout of the P
-//    operand; V is loaded with one 16-byte (or 8-byte) row chunk per lane and
-//    per token, and the output dims are permuted instead of transposing V
-//    (MFMA j, row m computes dim m * (D/16) + j).  No LDS on the hot loop.
+//    v_mfma_f32_16x16x16.  The K operand wants one token per lane column,
+//    which row loads do not give, so K rows go straight from HBM into a
+//    per-wave LDS tile (global_load_lds_dwordx4, no registers held while in
+//    flight), stored with an XOR swizzle of the 16-byte chunks so that the
+//    transposing ds_read_b128 of 16 different rows hits 16 different bank
+//    groups.  The score tile comes out with lane l holding tokens 4*(l/16)+i
+//    of head l%16, which is exactly the layout of the P operand; V rows are
+//    row loads already in the layout of the V^T operand (MFMA j, row m
+//    computes dim m * (D/16) + j).
 //
 // Block ids are prefetched 64 tiles at a time into one VGPR per wave and
-// read with v_readlane, so every K/V load is a scalar 64-bit block base plus
-// a 32-bit per-lane offset; the next tile's loads are issued before the
+// read with v_readlane, so every K/V address is a scalar 64-bit block base
+// plus a 32-bit per-lane offset; the next tile's loads are issued before the
 // current tile is computed.
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -43,9 +56,8 @@ namespace pa {
 namespace {
 
 constexpr int kTile = 16;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kPad = 4;  // LDS row padding (floats)
+constexpr int kMaxWaves = 8;
+constexpr int kMaxThreads = kMaxWaves * 64;
 
 template <int KIND>
 struct Esz {
@@ -62,6 +74,37 @@ __device__ __forceinline__ void store_out(void* out, int64_t off, float x) {
     static_cast<__bf16*>(out)[off] = (__bf16)x;
 }
 
+// N consecutive output elements from fp32 (N a multiple of 4), one store.
+template <int QK, int N>
+__device__ __forceinline__ void store_out_vec(void* out, int64_t off, const float* x) {
+  if constexpr (QK == K_F32) {
+#pragma unroll
+    for (int k = 0; k < N; k += 4)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(out) + off + k) =
+          f32x4{x[k], x[k + 1], x[k + 2], x[k + 3]};
+  } else {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k)
+      w[k] = QK == K_F16 ? pack_f16(x[2 * k], x[2 * k + 1]) : pack_bf16(x[2 * k], x[2 * k + 1]);
+    if constexpr (N == 4) {
+      *reinterpret_cast<i32x2*>(static_cast<uint16_t*>(out) + off) = i32x2{(int)w[0], (int)w[1]};
+    } else {
+#pragma unroll
+      for (int k = 0; k < N / 2; k += 4)
+        *reinterpret_cast<i32x4*>(static_cast<uint16_t*>(out) + off + 2 * k) =
+            i32x4{(int)w[k], (int)w[k + 1], (int)w[k + 2], (int)w[k + 3]};
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_f32_vec(float* dst, const float* x) {
+#pragma unroll
+  for (int k = 0; k < N; k += 4)
+    *reinterpret_cast<f32x4*>(dst + k) = f32x4{x[k], x[k + 1], x[k + 2], x[k + 3]};
+}
+
 // Sequence length clamped to what the block table can address (a longer
 // length is a caller error; clamping keeps every read inside the table).
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
@@ -70,16 +113,37 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// Physical block id of this wave's i-th tile (tiles w, w+4, w+8, ... of the
-// partition), 64 tiles per chunk.  Lane j of the chunk holds tile c*64+j.
-__device__ __forceinline__ int load_block_ids(const DecodeParams& p, int b, int t_lo,
-                                              int w, int chunk, int n_my) {
+// What one wave works on: its unit, sequence, partition and token range.
+struct Work {
+  int kvh, htile, b, part, L, t_lo, t_hi, n_tiles;
+};
+
+// false when the wave has nothing to do (unit past the end, or a partition
+// that starts beyond the sequence: its triple is never read).
+__device__ __forceinline__ bool wave_work(const DecodeParams& p, Work& wk) {
+  const int unit = blockIdx.x * p.waves + (threadIdx.x >> 6);
+  if (unit >= p.units) return false;
+  wk.kvh = unit / p.head_tiles;
+  wk.htile = unit - wk.kvh * p.head_tiles;
+  wk.b = blockIdx.z;
+  wk.part = blockIdx.y;
+  wk.L = clamp_len(p, wk.b);
+  wk.t_lo = wk.part * p.part_tokens;
+  if (wk.part > 0 && wk.t_lo >= wk.L) return false;
+  wk.t_hi = min(wk.L, wk.t_lo + p.part_tokens);
+  wk.n_tiles = wk.t_hi > wk.t_lo ? (wk.t_hi - wk.t_lo + kTile - 1) / kTile : 0;
+  return true;
+}
+
+// Physical block ids of tiles chunk*64 .. chunk*64+63 of the wave's range:
+// lane j holds the id of tile chunk*64 + j.
+__device__ __forceinline__ int load_block_ids(const DecodeParams& p, const Work& wk, int chunk) {
   const int lane = threadIdx.x & 63;
   const int i = chunk * 64 + lane;
   int id = 0;
-  if (i < n_my) {
-    const int t = t_lo + kTile * (w + kWaves * i);
-    id = p.tables[(int64_t)b * p.tab_stride + t / p.bs];
+  if (i < wk.n_tiles) {
+    const int t = wk.t_lo + kTile * i;
+    id = p.tables[(int64_t)wk.b * p.tab_stride + t / p.bs];
     // an id outside the pool is a caller error; read block 0 instead of
     // faulting
     if ((unsigned)id >= (unsigned)p.num_blocks) id = 0;
@@ -87,42 +151,125 @@ __device__ __forceinline__ int load_block_ids(const DecodeParams& p, int b, int 
   return id;
 }
 
-// Merge S softmax states per head from LDS and write the output row (or the
-// partition triple when the sequence spans several partitions).
-template <int QK, int D, int GT, int S>
-__device__ __forceinline__ void combine_and_store(const DecodeParams& p,
-                                                  const float (*ml)[GT][2],
-                                                  const float (*acc)[GT][D + kPad],
-                                                  int b, int part, int head0, int nh,
-                                                  int L) {
-  const bool triple = p.split && L > p.part_tokens;
-  for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
-    const int hh = idx / D;
-    const int d = idx - hh * D;
-    if (hh >= nh) continue;
-    float M = kMaxFloor;
-#pragma unroll
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s][hh][0]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const float sc = fast_exp2(ml[s][hh][0] - M);
-      den += ml[s][hh][1] * sc;
-      num += acc[s][hh][d] * sc;
-    }
-    const int h = head0 + hh;
-    if (triple) {
-      const int64_t base = ((int64_t)b * p.Hq + h) * p.num_parts + part;
-      p.ws_acc[base * D + d] = num;
-      if (d == 0) {
-        p.ws_ml[2 * base] = M;
-        p.ws_ml[2 * base + 1] = den;
-      }
-    } else {
-      const float o = den > 0.f ? num / den * p.v_scale : 0.f;
-      store_out<QK>(p.out, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d, o);
-    }
+// Byte offset of tile i inside the pool (block base + row offset in block);
+// `ids` holds the block ids of tiles (i & ~63) .. (i | 63).
+__device__ __forceinline__ int64_t tile_base(const DecodeParams& p, const Work& wk, int i,
+                                             int ids, int64_t blk_bytes, int64_t rs) {
+  const int blk = __builtin_amdgcn_readlane(ids, i & 63);
+  const int t0 = wk.t_lo + kTile * i;
+  return (int64_t)blk * blk_bytes + (int64_t)(t0 % p.bs) * rs;
+}
+
+// Two-stage software pipeline over tiles 0..n-1 with buffers A (even tiles)
+// and B (odd tiles): tile i + 2's loads are issued right after tile i is
+// computed.  In the steady state both next loads are unconditional, so at
+// every compute the loads still in flight are exactly the other buffer's,
+// and the compiler's wait before it is a count, not a full drain; the last
+// one to three tiles are peeled.
+template <class LA, class LB, class CA, class CB>
+__device__ __forceinline__ void run_pipeline(int base, int n, LA load_a, LB load_b, CA compute_a,
+                                             CB compute_b) {
+  if (n <= 0) return;
+  if (n == 1) {
+    load_a(base);
+    compute_a(base);
+    return;
   }
+  load_a(base);
+  load_b(base + 1);
+  int i = base;
+  const int end = base + n;
+  // sched_barrier keeps the compiler from sinking a stage's loads below the
+  // next compute (which would leave nothing in flight during it)
+  for (; i + 3 < end; i += 2) {
+    compute_a(i);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_b(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(i + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (i + 2 < end) {  // three left
+    compute_a(i);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_b(i + 1);
+    compute_a(i + 2);
+  } else {            // two left
+    compute_a(i);
+    compute_b(i + 1);
+  }
+}
+
+// Wait until every memory operation this wave has issued has completed
+// (s_waitcnt with all counters at zero).  The compiler does not reliably
+// order an LDS read after a load-to-LDS that fills the same bytes, so the
+// LDS tile reads below wait explicitly.
+__device__ __forceinline__ void wait_all_memory() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One-deep pipeline for kernels whose tiles pass through LDS by
+// load-to-LDS.  Tile i is read out of LDS into registers (fetch) after an
+// explicit full wait and before tile i + 1's loads are issued, so the wait
+// covers exactly tile i and tile i + 1's loads are in flight while tile i is
+// computed.
+template <class LA, class LB, class FA, class FB, class CA, class CB>
+__device__ __forceinline__ void run_pipeline_lds(int base, int n, LA load_a, LB load_b,
+                                                 FA fetch_a, FB fetch_b, CA compute_a,
+                                                 CB compute_b) {
+  if (n <= 0) return;
+  const int end = base + n;
+  load_a(base);
+  for (int i = base; i < end; i += 2) {
+    wait_all_memory();
+    fetch_a();
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 < end) load_b(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_a(i);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 1 >= end) break;
+    wait_all_memory();
+    fetch_b();
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 < end) load_a(i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_b(i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// All tiles of a wave's range: block ids are fetched 64 tiles at a time
+// (one lane each) and the pipeline runs over each 64-tile chunk.
+template <class LA, class LB, class CA, class CB>
+__device__ __forceinline__ void run_tiles(const DecodeParams& p, const Work& wk, int& ids,
+                                          LA load_a, LB load_b, CA compute_a, CB compute_b) {
+  for (int c0 = 0; c0 < wk.n_tiles; c0 += 64) {
+    ids = load_block_ids(p, wk, c0 >> 6);
+    run_pipeline(c0, min(64, wk.n_tiles - c0), load_a, load_b, compute_a, compute_b);
+  }
+}
+
+template <class LA, class LB, class FA, class FB, class CA, class CB>
+__device__ __forceinline__ void run_tiles_lds(const DecodeParams& p, const Work& wk, int& ids,
+                                              LA load_a, LB load_b, FA fetch_a, FB fetch_b,
+                                              CA compute_a, CB compute_b) {
+  for (int c0 = 0; c0 < wk.n_tiles; c0 += 64) {
+    ids = load_block_ids(p, wk, c0 >> 6);
+    run_pipeline_lds(c0, min(64, wk.n_tiles - c0), load_a, load_b, fetch_a, fetch_b, compute_a,
+                     compute_b);
+  }
+}
+
+// Triple slot of (sequence, query head, partition).
+__device__ __forceinline__ int64_t triple_index(const DecodeParams& p, int b, int h, int part) {
+  return ((int64_t)b * p.Hq + h) * p.num_parts + part;
 }
 
 // ============================================================================
@@ -130,43 +277,45 @@ __device__ __forceinline__ void combine_and_store(const DecodeParams& p,
 // of up to 16 query heads of one kv group.
 // ============================================================================
 template <int QK, int KVK, int D>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodeParams p) {
   constexpr bool kBF16 = QK == K_BF16;
   constexpr bool kFP8 = KVK == K_FP8;
   constexpr int ESZ = kFP8 ? 1 : 2;
-  constexpr int NJQ = D / 32;             // score MFMAs per tile (K = 32 dims each)
-  constexpr int NJV = D / 16;             // P x V MFMAs per tile; V elements per lane per token
-  constexpr int KLOADS = D * ESZ / 64;    // 16-byte K loads per lane per tile
-  constexpr int VBYTES = NJV * ESZ;       // V bytes per lane per token
-  constexpr int VW = NJV / 2;             // V words per token after conversion to 16-bit
-  static_assert(KLOADS >= 1 && (VBYTES == 16 || VBYTES == 8 || VBYTES == 4), "shape");
+  constexpr int RB = D * ESZ;          // bytes of one token's head row
+  constexpr int LR = RB / 16;          // 16-byte chunks per row
+  constexpr int TPI = 64 / LR;         // rows per 1 KiB load-to-LDS instruction
+  constexpr int NK = kTile / TPI;      // load-to-LDS instructions per tile
+  constexpr int SWZ = 256 / RB;        // consecutive rows sharing one swizzle
+  constexpr int NR = LR / 4;           // 16-byte LDS reads per lane per tile
+  constexpr int NJQ = D / 32;          // score MFMAs per tile (K = 32 dims each)
+  constexpr int NJV = D / 16;          // P x V MFMAs per tile; V elements per lane per token
+  constexpr int VBYTES = NJV * ESZ;    // V bytes per lane per token
+  constexpr int VW = NJV / 2;          // V words per token after conversion to 16-bit
+  constexpr int SLOTS = kTile * LR;    // 16-byte LDS slots per tile
+  static_assert(NK >= 1 && NR >= 1 && (kFP8 ? 2 * NR == NJQ : NR == NJQ), "shape");
+  static_assert(VBYTES == 16 || VBYTES == 8 || VBYTES == 4, "shape");
 
-  __shared__ float sm_ml[kWaves][16][2];
-  __shared__ float sm_acc[kWaves][16][D + kPad];
+  // two K tiles per wave, in two arrays so the compiler can tell the
+  // in-flight tile's LDS writes from the current tile's reads
+  __shared__ i32x4 kt0[kMaxWaves][SLOTS];
+  __shared__ i32x4 kt1[kMaxWaves][SLOTS];
 
+  Work wk;
+  if (!wave_work(p, wk)) return;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int b = blockIdx.z;
-  const int part = blockIdx.y;
-  const int kvh = blockIdx.x / p.head_tiles;
-  const int htile = blockIdx.x - kvh * p.head_tiles;
-  const int L = clamp_len(p, b);
-  const int t_lo = part * p.part_tokens;
-  if (part > 0 && t_lo >= L) return;  // whole workgroup: nothing in this partition
-  const int t_hi = min(L, t_lo + p.part_tokens);
-  const int n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTile - 1) / kTile : 0;
-  const int n_my = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
-  const int gh0 = htile * 16;
+  const int gh0 = wk.htile * 16;
   const int nh = min(16, p.G - gh0);
-  const int head0 = kvh * p.G + gh0;
+  const int head0 = wk.kvh * p.G + gh0;
 
-  // Query group as the B operand of the score MFMAs: lane (n, g) holds head n,
-  // 8 dims per MFMA.  The dims a lane contributes must match the K operand.
+  // Query group as the B operand of the score MFMAs: lane (n, g) holds head
+  // n, 8 dims per MFMA: those of 16-byte K chunk 4r + g (16-bit K: MFMA r;
+  // fp8 K: the low / high half of that chunk for MFMAs 2r, 2r + 1).
   i32x4 qop[NJQ];
   {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)b * p.q_sb +
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)wk.b * p.q_sb +
                            (int64_t)(head0 + min(n, nh - 1)) * p.q_sh;
 #pragma unroll
     for (int j = 0; j < NJQ; ++j) {
@@ -176,38 +325,41 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
     }
   }
 
-  const int64_t rs = (int64_t)p.Hkv * D * ESZ;  // bytes between tokens
+  const int64_t rs = (int64_t)p.Hkv * RB;  // bytes between tokens
   const int64_t blk_bytes = rs * p.bs;
-  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
-  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
-  // K: lane (token n, group g) reads 16 bytes at jl*64 + g*16 of its token row.
-  // V: lane (dim chunk n, group g) reads VBYTES at n*VBYTES of tokens 4g+i.
-  uint32_t koff[KLOADS];
+  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)wk.kvh * RB;
+  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)wk.kvh * RB;
+  // K to LDS: instruction j, lane l loads row tt = j*TPI + l/LR, chunk
+  // (l % LR) ^ swz(tt), landing in slot tt*LR + l%LR; so slot tt*LR + s
+  // holds chunk s ^ swz(tt) of row tt.
+  uint32_t kdma[NK];
 #pragma unroll
-  for (int jl = 0; jl < KLOADS; ++jl) koff[jl] = (uint32_t)(n * rs + jl * 64 + g * 16);
+  for (int j = 0; j < NK; ++j) {
+    const int tt = j * TPI + lane / LR;
+    const int ch = (lane % LR) ^ ((tt / SWZ) % LR);
+    kdma[j] = (uint32_t)(tt * rs + ch * 16);
+  }
+  // K operand reads: lane (n, g), read r wants chunk 4r + g of row n
+  int kslot[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) kslot[r] = n * LR + ((4 * r + g) ^ ((n / SWZ) % LR));
+  // V: lane (dim chunk n, group g) reads VBYTES at n*VBYTES of tokens 4g+i.
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * g + i) * rs + n * VBYTES);
 
   struct Regs {
-    Bytes<16> k[KLOADS];
     Bytes<VBYTES> v[4];
   };
 
-  int ids = 0, ids_chunk = -1;
-  auto load_tile = [&](int i, Regs& r) {
-    const int c = i >> 6;
-    if (c != ids_chunk) {
-      ids = load_block_ids(p, b, t_lo, w, c, n_my);
-      ids_chunk = c;
-    }
-    const int blk = __builtin_amdgcn_readlane(ids, i & 63);
-    const int t0 = t_lo + kTile * (w + kWaves * i);
-    const int64_t tb = (int64_t)blk * blk_bytes + (int64_t)(t0 % p.bs) * rs;
+  int ids = 0;
+  auto load_tile = [&](int i, i32x4* kt, Regs& r) {
+    const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
     const char* kb = kbase + tb;
     const char* vb = vbase + tb;
 #pragma unroll
-    for (int jl = 0; jl < KLOADS; ++jl) r.k[jl] = load_bytes<16>(kb, koff[jl]);
+    for (int j = 0; j < NK; ++j)
+      load_lds16(kb + kdma[j], kt + j * 64);
 #pragma unroll
     for (int q = 0; q < 4; ++q) r.v[q] = load_bytes<VBYTES>(vb, voff[q]);
   };
@@ -218,35 +370,35 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
 #pragma unroll
   for (int j = 0; j < NJV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_tile = [&](int i, Regs& r) {
-    const int t0 = t_lo + kTile * (w + kWaves * i);
-    if (t0 + kTile > t_hi) {
-      // tokens past the end of the sequence may hold anything (NaN poison):
-      // their V rows must not reach the P x V product
+  // K operand chunks of the tile in LDS
+  i32x4 kreg[NR];
+  auto fetch_tile = [&](const i32x4* kt) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (t0 + 4 * g + q >= t_hi) r.v[q].zero();
-    }
+    for (int rr = 0; rr < NR; ++rr) kreg[rr] = kt[kslot[rr]];
+  };
+
+  auto compute_tile = [&](int i, Regs& r) {
+    const int t0 = wk.t_lo + kTile * i;
     // scores: D[token 4g+q][head n]
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < NJQ; ++j) {
-      i32x4 a;
+    for (int rr = 0; rr < NR; ++rr) {
+      const i32x4 kc = kreg[rr];
       if constexpr (kFP8) {
-        const uint32_t w0 = r.k[j >> 1].w((j & 1) * 2);
-        const uint32_t w1 = r.k[j >> 1].w((j & 1) * 2 + 1);
-        const i32x2 lo = kBF16 ? fp8x4_to_bf16x4(w0) : fp8x4_to_f16x4(w0);
-        const i32x2 hi = kBF16 ? fp8x4_to_bf16x4(w1) : fp8x4_to_f16x4(w1);
-        a = i32x4{lo[0], lo[1], hi[0], hi[1]};
+        const i32x2 c0 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[0]) : fp8x4_to_f16x4((uint32_t)kc[0]);
+        const i32x2 c1 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[1]) : fp8x4_to_f16x4((uint32_t)kc[1]);
+        const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[2]) : fp8x4_to_f16x4((uint32_t)kc[2]);
+        const i32x2 c3 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[3]) : fp8x4_to_f16x4((uint32_t)kc[3]);
+        s = mfma_k32<kBF16>(i32x4{c0[0], c0[1], c1[0], c1[1]}, qop[2 * rr], s);
+        s = mfma_k32<kBF16>(i32x4{c2[0], c2[1], c3[0], c3[1]}, qop[2 * rr + 1], s);
       } else {
-        a = r.k[j].v;
+        s = mfma_k32<kBF16>(kc, qop[rr], s);
       }
-      s = mfma_k32<kBF16>(a, qop[j], s);
     }
     float sv[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      sv[q] = (t0 + 4 * g + q < t_hi) ? s[q] * p.qk_scale_log2 : -INFINITY;
+      sv[q] = (t0 + 4 * g + q < wk.t_hi) ? s[q] * p.qk_scale_log2 : -INFINITY;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -263,20 +415,24 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
     m = m_new;
     const i32x2 pop = {(int)pw0, (int)pw1};
 
-    // V rows as 16-bit words: vw[q][k] holds elements 2k, 2k+1 of token 4g+q
+    // V rows as 16-bit words: vw[q][k] holds elements 2k, 2k+1 of token 4g+q.
+    // Tokens past the end of the sequence may hold anything (NaN poison):
+    // their rows are replaced by zeros (a select, not a branch, so the loads
+    // still in flight are not waited for) before the P x V product.
     uint32_t vw[4][VW];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      const bool ok = t0 + 4 * g + q < wk.t_hi;
       if constexpr (kFP8) {
 #pragma unroll
         for (int k = 0; k < VW / 2; ++k) {
           const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4(r.v[q].w(k)) : fp8x4_to_f16x4(r.v[q].w(k));
-          vw[q][2 * k] = (uint32_t)c2[0];
-          vw[q][2 * k + 1] = (uint32_t)c2[1];
+          vw[q][2 * k] = ok ? (uint32_t)c2[0] : 0u;
+          vw[q][2 * k + 1] = ok ? (uint32_t)c2[1] : 0u;
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < VW; ++k) vw[q][k] = r.v[q].w(k);
+        for (int k = 0; k < VW; ++k) vw[q][k] = ok ? r.v[q].w(k) : 0u;
       }
     }
 #pragma unroll
@@ -295,41 +451,55 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(const DecodeParam
     }
   };
 
-  // two register sets in ping-pong: the next tile's loads are in flight
-  // while the current tile is computed
-  if (n_my > 0) {
+  // two K tiles in LDS and two V register sets in ping-pong: the next
+  // tile's loads are in flight while the current tile is computed
+  {
     Regs r0, r1;
-    load_tile(0, r0);
-    int i = 0;
-    for (; i + 1 < n_my; i += 2) {
-      load_tile(i + 1, r1);
-      compute_tile(i, r0);
-      if (i + 2 < n_my) load_tile(i + 2, r0);
-      compute_tile(i + 1, r1);
-    }
-    if (i < n_my) compute_tile(i, r0);
+    run_tiles_lds(
+        p, wk, ids, [&](int i) { load_tile(i, kt0[w], r0); },
+        [&](int i) { load_tile(i, kt1[w], r1); }, [&]() { fetch_tile(kt0[w]); },
+        [&]() { fetch_tile(kt1[w]); }, [&](int i) { compute_tile(i, r0); },
+        [&](int i) { compute_tile(i, r1); });
   }
 
   // lane groups hold partial sums over different tokens
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (g == 0) {
-    sm_ml[w][n][0] = m;
-    sm_ml[w][n][1] = l;
+  if (n >= nh) return;
+  const int h = head0 + n;
+  // lane (n, g) holds out[h][(4g+i)*NJV + j] in acc[j][i]
+  const bool triple = p.split && wk.L > p.part_tokens;
+  if (triple) {
+    const int64_t ti = triple_index(p, wk.b, h, wk.part);
+    if (g == 0) {
+      p.ws_ml[2 * ti] = m;
+      p.ws_ml[2 * ti + 1] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[NJV];
+#pragma unroll
+      for (int j = 0; j < NJV; ++j) x[j] = acc[j][i];
+      store_f32_vec<NJV>(p.ws_acc + ti * D + (4 * g + i) * NJV, x);
+    }
+  } else {
+    const float sc = l > 0.f ? p.v_scale / l : 0.f;
+    const int64_t ob = (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x[NJV];
+#pragma unroll
+      for (int j = 0; j < NJV; ++j) x[j] = acc[j][i] * sc;
+      store_out_vec<QK, NJV>(p.out, ob + (4 * g + i) * NJV, x);
+    }
   }
-#pragma unroll
-  for (int j = 0; j < NJV; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) sm_acc[w][n][(4 * g + q) * NJV + j] = acc[j][q];
-  __syncthreads();
-  combine_and_store<QK, D, 16, kWaves>(p, sm_ml, sm_acc, b, part, head0, nh, L);
 }
 
 // ============================================================================
-// VALU inner loop: any supported dtype pair, GT query heads per workgroup.
+// VALU inner loop: any supported dtype pair, GT query heads per wave.
 // ============================================================================
 template <int QK, int KVK, int D, int GT>
-__global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kMaxThreads) void decode_valu_kernel(const DecodeParams p) {
   constexpr int ESZ = Esz<KVK>::v;
   constexpr int VEC = 16 / ESZ;      // KV elements per 16-byte load
   constexpr int LPT = D / VEC;       // lanes per token row
@@ -339,27 +509,16 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   constexpr int QE = VEC;            // query elements per lane
   static_assert(LPT >= 1 && LPT <= 64 && 64 % LPT == 0 && kTile % TPL == 0, "shape");
   static_assert(!kDot2 || QK == KVK, "16-bit KV needs a query of the same type");
+  static_assert(VEC % 4 == 0, "shape");
 
-  __shared__ float sm_ml[kWaves][GT][2];
-  __shared__ float sm_acc[kWaves][GT][D + kPad];
-
+  Work wk;
+  if (!wave_work(p, wk)) return;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
   const int r = lane / LPT;          // token slot of this lane in a load
   const int c = lane - r * LPT;      // 16-byte chunk of the row
-  const int b = blockIdx.z;
-  const int part = blockIdx.y;
-  const int kvh = blockIdx.x / p.head_tiles;
-  const int htile = blockIdx.x - kvh * p.head_tiles;
-  const int L = clamp_len(p, b);
-  const int t_lo = part * p.part_tokens;
-  if (part > 0 && t_lo >= L) return;
-  const int t_hi = min(L, t_lo + p.part_tokens);
-  const int n_tiles = t_hi > t_lo ? (t_hi - t_lo + kTile - 1) / kTile : 0;
-  const int n_my = n_tiles > w ? (n_tiles - w + kWaves - 1) / kWaves : 0;
-  const int gh0 = htile * GT;
+  const int gh0 = wk.htile * GT;
   const int nh = min(GT, p.G - gh0);
-  const int head0 = kvh * p.G + gh0;
+  const int head0 = wk.kvh * p.G + gh0;
 
   // query chunk of each head: packed 16-bit words for v_dot2, else fp32
   // pre-multiplied by the score scale
@@ -368,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
 #pragma unroll
   for (int gh = 0; gh < GT; ++gh) {
     const int hq = head0 + min(gh, nh - 1);
-    const int64_t qo = (int64_t)b * p.q_sb + (int64_t)hq * p.q_sh + c * QE;
+    const int64_t qo = (int64_t)wk.b * p.q_sb + (int64_t)hq * p.q_sh + c * QE;
     if constexpr (kDot2) {
       const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + qo);
 #pragma unroll
@@ -400,8 +559,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
 
   const int64_t rs = (int64_t)p.Hkv * D * ESZ;
   const int64_t blk_bytes = rs * p.bs;
-  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
-  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
+  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)wk.kvh * D * ESZ;
+  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)wk.kvh * D * ESZ;
   uint32_t off[NL];
 #pragma unroll
   for (int li = 0; li < NL; ++li) off[li] = (uint32_t)((li * TPL + r) * rs + c * 16);
@@ -410,16 +569,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     Bytes<16> k[NL];
     Bytes<16> v[NL];
   };
-  int ids = 0, ids_chunk = -1;
+  int ids = 0;
   auto load_tile = [&](int i, Regs& rg) {
-    const int ch = i >> 6;
-    if (ch != ids_chunk) {
-      ids = load_block_ids(p, b, t_lo, w, ch, n_my);
-      ids_chunk = ch;
-    }
-    const int blk = __builtin_amdgcn_readlane(ids, i & 63);
-    const int t0 = t_lo + kTile * (w + kWaves * i);
-    const int64_t tb = (int64_t)blk * blk_bytes + (int64_t)(t0 % p.bs) * rs;
+    const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
 #pragma unroll
     for (int li = 0; li < NL; ++li) rg.k[li] = load_bytes<16>(kbase + tb, off[li]);
 #pragma unroll
@@ -436,18 +588,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
   }
 
   auto compute_tile = [&](int i, Regs& rg) {
-    const int t0 = t_lo + kTile * (w + kWaves * i);
+    const int t0 = wk.t_lo + kTile * i;
+    // tokens past the end of the sequence may hold anything (NaN poison):
+    // their scores become -inf and their V rows zeros, by selects (not
+    // branches, so the loads still in flight are not waited for)
     bool valid[NL];
 #pragma unroll
-    for (int li = 0; li < NL; ++li) valid[li] = t0 + li * TPL + r < t_hi;
-    if (t0 + kTile > t_hi) {
-#pragma unroll
-      for (int li = 0; li < NL; ++li)
-        if (!valid[li]) {
-          rg.k[li].zero();
-          rg.v[li].zero();
-        }
-    }
+    for (int li = 0; li < NL; ++li) valid[li] = t0 + li * TPL + r < wk.t_hi;
     // scores (log2 units) of the NL tokens this row holds
     float sc[GT][NL];
 #pragma unroll
@@ -487,7 +634,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
     for (int li = 0; li < NL; ++li) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t wd = rg.v[li].w(k);
+        const uint32_t wd = valid[li] ? rg.v[li].w(k) : 0u;
         if constexpr (KVK == K_F32) {
           vf[li][k] = __builtin_bit_cast(float, wd);
         } else if constexpr (KVK == K_F16) {
@@ -533,20 +680,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
 
   // two register sets in ping-pong: the next tile's loads are in flight
   // while the current tile is computed
-  if (n_my > 0) {
+  {
     Regs r0, r1;
-    load_tile(0, r0);
-    int i = 0;
-    for (; i + 1 < n_my; i += 2) {
-      load_tile(i + 1, r1);
-      compute_tile(i, r0);
-      if (i + 2 < n_my) load_tile(i + 2, r0);
-      compute_tile(i + 1, r1);
-    }
-    if (i < n_my) compute_tile(i, r0);
+    run_tiles(
+        p, wk, ids, [&](int i) { load_tile(i, r0); }, [&](int i) { load_tile(i, r1); },
+        [&](int i) { compute_tile(i, r0); }, [&](int i) { compute_tile(i, r1); });
   }
 
-  // rows of one wave hold disjoint tokens: merge their states (lanes with the
+  // rows of the wave hold disjoint tokens: merge their states (lanes with the
   // same chunk c sit LPT, 2*LPT, ... lanes apart)
 #pragma unroll
   for (int step = LPT; step < 64; step <<= 1) {
@@ -566,19 +707,27 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(const DecodeParam
       m[gh] = mm;
     }
   }
-  if (r == 0) {
+  if (r != 0) return;
+  const bool triple = p.split && wk.L > p.part_tokens;
 #pragma unroll
-    for (int gh = 0; gh < GT; ++gh) {
+  for (int gh = 0; gh < GT; ++gh) {
+    if (gh >= nh) break;
+    const int h = head0 + gh;
+    if (triple) {
+      const int64_t ti = triple_index(p, wk.b, h, wk.part);
       if (c == 0) {
-        sm_ml[w][gh][0] = m[gh];
-        sm_ml[w][gh][1] = lsum[gh];
+        p.ws_ml[2 * ti] = m[gh];
+        p.ws_ml[2 * ti + 1] = lsum[gh];
       }
+      store_f32_vec<VEC>(p.ws_acc + ti * D + c * VEC, acc[gh]);
+    } else {
+      const float sc = lsum[gh] > 0.f ? p.v_scale / lsum[gh] : 0.f;
+      float x[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) sm_acc[w][gh][c * VEC + e] = acc[gh][e];
+      for (int e = 0; e < VEC; ++e) x[e] = acc[gh][e] * sc;
+      store_out_vec<QK, VEC>(p.out, (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh + c * VEC, x);
     }
   }
-  __syncthreads();
-  combine_and_store<QK, D, GT, kWaves>(p, sm_ml, sm_acc, b, part, head0, nh, L);
 }
 
 // ============================================================================
@@ -593,7 +742,7 @@ __global__ __launch_bounds__(D) void merge_kernel(const DecodeParams p) {
   const int L = clamp_len(p, b);
   if (L <= p.part_tokens) return;  // single partition: written directly
   const int P = (L + p.part_tokens - 1) / p.part_tokens;
-  const int64_t base = ((int64_t)b * p.Hq + h) * p.num_parts;
+  const int64_t base = triple_index(p, b, h, 0);
   const float* ml = p.ws_ml + 2 * base;
   const float* acc = p.ws_acc + base * D + d;
   float M = kMaxFloor;
@@ -615,31 +764,31 @@ hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
 }
 
 template <int QK, int KVK, int D>
-hipError_t launch_valu(const DecodeParams& p, int gt, dim3 grid, hipStream_t stream) {
+hipError_t launch_valu(const DecodeParams& p, int gt, dim3 grid, dim3 block, hipStream_t stream) {
   switch (gt) {
-    case 1: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 1>), grid, dim3(kThreads), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 2>), grid, dim3(kThreads), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 4>), grid, dim3(kThreads), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 1>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 2>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_valu_kernel<QK, KVK, D, 4>), grid, block, 0, stream, p); break;
     default: return hipErrorNotSupported;
   }
   return hipGetLastError();
 }
 
 template <int QK, int KVK, int D>
-hipError_t launch_mfma(const DecodeParams& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_mfma_kernel<QK, KVK, D>), grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <int QK, int KVK, int D>
 hipError_t launch_all(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {
-  const dim3 grid(p.Hkv * p.head_tiles, p.num_parts, p.B);
+  if (p.waves < 1 || p.waves > kMaxWaves) return hipErrorInvalidValue;
+  const dim3 grid((p.units + p.waves - 1) / p.waves, p.num_parts, p.B);
+  const dim3 block(p.waves * 64);
   hipError_t e;
   if (v.path == 2) {
-    if constexpr (QK == K_F32 || KVK == K_F32) return hipErrorNotSupported;
-    else e = launch_mfma<QK, KVK, D>(p, grid, stream);
+    if constexpr (QK == K_F32 || KVK == K_F32) {
+      return hipErrorNotSupported;
+    } else {
+      hipLaunchKernelGGL((decode_mfma_kernel<QK, KVK, D>), grid, block, 0, stream, p);
+      e = hipGetLastError();
+    }
   } else {
-    e = launch_valu<QK, KVK, D>(p, v.gt, grid, stream);
+    e = launch_valu<QK, KVK, D>(p, v.gt, grid, block, stream);
   }
   if (e != hipSuccess) return e;
   if (p.split) return launch_merge<QK, D>(p, stream);
@@ -666,6 +815,8 @@ bool decode_variant_built(const DecodeVariant& v) {
   if (v.path == 1) return v.gt == 1 || v.gt == 2 || v.gt == 4;
   return false;
 }
+
+int decode_max_waves() { return kMaxWaves; }
 
 hipError_t launch_decode(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {
   if (!decode_variant_built(v)) return hipErrorNotSupported;

@@ -146,6 +146,10 @@ struct Bytes<4> {
   __device__ __forceinline__ void zero() { v = 0; }
 };
 
+// cache-policy operand of the load-to-LDS builtin that marks a load
+// non-temporal
+constexpr int kNonTemporalAux = 2;
+
 // K/V rows are read exactly once per decode call: non-temporal loads keep
 // them from displacing reusable lines in the caches (on MI355X this lifts a
 // paged gather from ~5.9 to ~6.4 TB/s).
@@ -159,6 +163,16 @@ __device__ __forceinline__ Bytes<BYTES> load_bytes(const char* base, uint32_t of
   else
     r.v = __builtin_nontemporal_load(reinterpret_cast<const int*>(base + off));
   return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds_base + 16 * l; the
+// LDS base must be the same for the whole wave.  Non-temporal like the
+// register loads above.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   kNonTemporalAux);
 }
 
 }  // namespace pa

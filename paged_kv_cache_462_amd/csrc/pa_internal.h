@@ -25,6 +25,8 @@ struct DecodeParams {
   int32_t B, Hq, Hkv, G, D, bs, max_blocks;
   int32_t num_blocks;     // physical pool size
   int32_t head_tiles;     // ceil(G / tile heads)
+  int32_t units;          // Hkv * head_tiles: one wave each per partition
+  int32_t waves;          // waves per workgroup (consecutive units)
   int32_t part_tokens;    // tokens per partition (multiple of 16)
   int32_t num_parts;      // partitions per sequence in the grid (>= 1)
   int32_t split;          // 1: write triples and merge afterwards
@@ -74,5 +76,8 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 
 // Variants built into this library (for pa_build_info / validation).
 bool decode_variant_built(const DecodeVariant& v);
+
+// Largest number of work units (waves) one decode workgroup holds.
+int decode_max_waves();
 
 }  // namespace pa
