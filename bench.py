@@ -181,8 +181,8 @@ def main() -> int:
     ws_bytes = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                          c.block_size, wl.max_blocks, args.partition_tokens)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    part = pa.decode_plan_partition(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                    c.block_size, wl.max_blocks, args.partition_tokens)
+    plan = pa.decode_plan(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                          c.block_size, wl.max_blocks, args.partition_tokens)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -235,11 +235,11 @@ def main() -> int:
     kv_logical = wl.logical_kv_bytes()
     gbps_step = kv_unique / (ms_step * 1e-3) / 1e9
     achieved = kv_unique / (dec_mean * 1e-3) / 1e9
-    launch_desc = f"partition={part} path={args.path}"
+    launch_desc = f"schedule={plan['schedule']} partition={plan['partition_tokens']} path={args.path}"
     traffic = load_traffic(c.name, launch_desc)
     roof = {
         "bound": "hbm",
-        "kernel": "pa_decode" + (" (partition + merge kernels)" if part else ""),
+        "kernel": "pa_decode" + (" (decode + merge kernels)" if plan["schedule"] != "single" else ""),
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
@@ -276,7 +276,8 @@ def main() -> int:
             "sum_seq_len": int(wl.seq_lens.astype(np.int64).sum()),
             "q_dtype": c.q_dtype,
             "kv_dtype": c.kv_dtype,
-            "partition_tokens": part,
+            "schedule": plan["schedule"],
+            "partition_tokens": plan["partition_tokens"],
             "path": {0: "auto", 1: "valu", 2: "mfma"}[args.path],
             "kv_bytes_unique": kv_unique,
             "kv_bytes_logical": kv_logical,

@@ -86,9 +86,9 @@ typedef struct pa_launch {
   void* stream;             /* hipStream_t; NULL = null stream                   */
   void* workspace;          /* device scratch for split decode, caller-owned     */
   size_t workspace_bytes;   /* its size                                          */
-  int32_t partition_tokens; /* 0 = automatic; -1 = never split; > 0: split each
-                               sequence into partitions of this many tokens
-                               (a multiple of 16)                                */
+  int32_t partition_tokens; /* 0 = automatic (see pa_decode_plan); -1 = never
+                               split; > 0: split each sequence into partitions
+                               of this many tokens (a multiple of 16)            */
   int32_t path;             /* PA_PATH_*                                         */
 } pa_launch;
 
@@ -132,9 +132,10 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
  *   launch        stream, workspace (16-byte aligned) and partitioning;
  *                 NULL = null stream, automatic partitioning, no workspace
  * Supported head_dim: 64, 128.  When the chosen plan splits sequences into
- * partitions, per-partition (max, sum, partial output) triples go to the
- * workspace and a second kernel merges them; pa_decode_workspace_bytes
- * gives the size.  Results are deterministic (no atomics).
+ * pieces, per-piece (max, sum, partial output) triples go to the workspace
+ * and a second kernel merges them; pa_decode_workspace_bytes gives the size
+ * (pa_decode_plan describes the plan).  Results are deterministic (no
+ * atomics) for a given plan.
  */
 int pa_decode(pa_tensor* out, const pa_tensor* query,
               const pa_tensor* key_cache, const pa_tensor* value_cache,
@@ -164,13 +165,29 @@ int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                   int32_t block_size, int32_t max_blocks,
                                   int32_t partition_tokens);
 
+/* how pa_decode spreads the work (pa_decode_plan) */
+#define PA_SCHEDULE_SINGLE 0     /* one workgroup per sequence                 */
+#define PA_SCHEDULE_PARTITIONS 1 /* fixed-size token partitions, then a merge  */
+#define PA_SCHEDULE_BALANCED 2   /* equal shares of the batch's 16-token tiles
+                                    per workgroup (256 per unit chunk), found
+                                    on the device from seq_lens; sequences cut
+                                    by a share boundary are merged afterwards */
+
+typedef struct pa_decode_plan_info {
+  int32_t schedule;         /* PA_SCHEDULE_*                                    */
+  int32_t partition_tokens; /* PA_SCHEDULE_PARTITIONS: tokens per partition     */
+  int64_t workspace_bytes;  /* what pa_decode_workspace_bytes returns           */
+} pa_decode_plan_info;
+
 /*
- * Partition size pa_decode would use (tokens; 0 = no split) for these sizes.
+ * The plan pa_decode makes for these sizes and this partition request:
+ * partition_tokens 0 (automatic) picks the balanced schedule when
+ * batch <= 2048, else 512-token partitions; -1 never splits; > 0 asks for
+ * partitions of that many tokens.  Returns PA_OK or a negative status.
  */
-int32_t pa_decode_plan_partition(int32_t batch, int32_t num_q_heads,
-                                 int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t block_size, int32_t max_blocks,
-                                 int32_t partition_tokens);
+int pa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                   int32_t partition_tokens, pa_decode_plan_info* info);
 
 /* Thread-local message for the last failing call on this thread. */
 const char* pa_last_error(void);

@@ -16,7 +16,7 @@ from .ops import (  # noqa: F401
     build_info,
     copy_blocks,
     decode,
-    decode_plan_partition,
+    decode_plan,
     decode_workspace_bytes,
     reshape_and_cache,
 )

@@ -36,6 +36,13 @@ class PaTensor(ctypes.Structure):
                 ("shape", c_int64 * 4), ("stride", c_int64 * 4), ("scale", c_float)]
 
 
+class PaDecodePlan(ctypes.Structure):
+    _fields_ = [("schedule", c_int32), ("partition_tokens", c_int32), ("workspace_bytes", c_int64)]
+
+
+PA_SCHEDULE_SINGLE, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED = 0, 1, 2
+
+
 class PaLaunch(ctypes.Structure):
     _fields_ = [("stream", c_void_p), ("workspace", c_void_p),
                 ("workspace_bytes", c_size_t), ("partition_tokens", c_int32),
@@ -52,7 +59,7 @@ SIGNATURES = {
     "pa_decode": (c_int32, [_T, _T, _T, _T, _T, _T, c_float, c_int32, c_int32, _L]),
     "pa_copy_blocks": (c_int32, [_T, _T, _T, _L]),
     "pa_decode_workspace_bytes": (c_int64, [c_int32] * 7),
-    "pa_decode_plan_partition": (c_int32, [c_int32] * 7),
+    "pa_decode_plan": (c_int32, [c_int32] * 7 + [POINTER(PaDecodePlan)]),
     "pa_last_error": (c_char_p, []),
     "pa_build_info": (c_char_p, []),
     "pa_alloc_create": (_A, [c_int32, POINTER(c_int32)]),

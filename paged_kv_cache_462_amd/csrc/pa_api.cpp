@@ -91,15 +91,18 @@ int check_cache_pair(const pa_tensor* k, const pa_tensor* v) {
 }
 
 struct Plan {
+  int sched = pa::kSchedFixed;
   int split = 0;
   int part_tokens = 0;
   int num_parts = 1;
+  int64_t slots = 0;     // triple slots in the workspace
   int64_t ws_bytes = 0;
 };
 
-// Shared by pa_decode and the workspace query.  The host never reads
-// seq_lens (they live on the device), so the grid covers the table width;
-// partitions past a sequence's end exit at once.
+// Shared by pa_decode and the plan / workspace queries.  The host never
+// reads seq_lens (they live on the device): the balanced schedule finds the
+// lengths on the device, and a fixed split covers the table width (its
+// partitions past a sequence's end exit at once).
 int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
@@ -109,22 +112,31 @@ int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Pl
   const int64_t max_ctx64 = (int64_t)max_blocks * bs;
   if (max_ctx64 > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "block table addresses too many tokens");
   const int max_ctx = (int)max_ctx64;
+  if (req > 0 && req % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of 16");
+  if (req < -1) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be -1, 0 or positive");
   Plan p;
-  int pt = req;
-  if (pt == 0) pt = 512;  // automatic: 512-token partitions for long contexts
-  if (pt > 0 && pt % 16) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be a multiple of 16");
-  if (pt < -1) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be -1, 0 or positive");
-  if (pt == -1 || pt >= max_ctx) {
-    p.split = 0;
-    p.part_tokens = max_ctx > 0 ? ((max_ctx + 15) / 16) * 16 : 16;
-    p.num_parts = 1;
-  } else {
+  const int64_t max_tiles = (int64_t)B * ((max_ctx + 15) / 16);
+  if (req == 0 && B <= pa::kBalancedMaxBatch && max_tiles < (int64_t)1 << 30) {
+    // automatic: equal shares of the batch's tiles per workgroup
+    p.sched = pa::kSchedBalanced;
     p.split = 1;
-    p.part_tokens = pt;
-    p.num_parts = (max_ctx + pt - 1) / pt;
-    if (p.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", p.num_parts);
-    p.ws_bytes = (int64_t)B * Hq * p.num_parts * (D + 2) * (int64_t)sizeof(float);
+    p.slots = (int64_t)pa::kBalancedWorkgroups + B;
+  } else {
+    const int pt = req == 0 ? 512 : req;  // automatic fallback: 512-token partitions
+    if (pt == -1 || pt >= max_ctx) {
+      p.part_tokens = max_ctx > 0 ? ((max_ctx + 15) / 16) * 16 : 16;
+    } else {
+      p.split = 1;
+      p.part_tokens = pt;
+      p.num_parts = (max_ctx + pt - 1) / pt;
+      if (p.num_parts > 65535) return fail(PA_ERR_UNSUPPORTED, "too many partitions (%d)", p.num_parts);
+      p.slots = (int64_t)B * p.num_parts;
+    }
   }
+  // workspace: acc [slots, Hq, D] f32, then (max, sum) [slots, Hq, 2] f32,
+  // then per-sequence (first slot, pieces) [B, 2] i32 (balanced only)
+  p.ws_bytes = p.slots * Hq * (D + 2) * (int64_t)sizeof(float) +
+               (p.sched == pa::kSchedBalanced ? (int64_t)B * 2 * (int64_t)sizeof(int32_t) : 0);
   *out = p;
   return PA_OK;
 }
@@ -150,13 +162,20 @@ int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
   return rc ? rc : p.ws_bytes;
 }
 
-int32_t pa_decode_plan_partition(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, int32_t max_blocks,
-                                 int32_t partition_tokens) {
+int pa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t max_blocks, int32_t partition_tokens,
+                   pa_decode_plan_info* info) {
+  if (!info) return fail(PA_ERR_INVALID_ARG, "null plan descriptor");
   Plan p;
   int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
                      partition_tokens, &p);
-  return rc ? rc : (p.split ? p.part_tokens : 0);
+  if (rc) return rc;
+  info->schedule = p.sched == pa::kSchedBalanced ? PA_SCHEDULE_BALANCED
+                   : p.split                     ? PA_SCHEDULE_PARTITIONS
+                                                 : PA_SCHEDULE_SINGLE;
+  info->partition_tokens = p.sched == pa::kSchedBalanced || !p.split ? 0 : p.part_tokens;
+  info->workspace_bytes = p.ws_bytes;
+  return PA_OK;
 }
 
 int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
@@ -259,6 +278,12 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   if (units > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   p.units = (int)units;
   p.waves = (int)(units < pa::decode_max_waves() ? units : pa::decode_max_waves());
+  {
+    const int chunks = (p.units + p.waves - 1) / p.waves;
+    const int nwc = pa::kBalancedWorkgroups / chunks;
+    p.nwc = nwc < 1 ? 1 : nwc;
+  }
+  p.sched = plan.sched;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
@@ -267,7 +292,8 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
   if (plan.split) {
     p.ws_acc = static_cast<float*>(launch->workspace);
-    p.ws_ml = p.ws_acc + (int64_t)B * Hq * plan.num_parts * D;
+    p.ws_ml = p.ws_acc + plan.slots * Hq * D;
+    p.ws_meta = reinterpret_cast<int32_t*>(p.ws_ml + plan.slots * Hq * 2);
   }
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_decode(p, v, stream);

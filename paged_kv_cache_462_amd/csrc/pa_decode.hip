@@ -11,19 +11,28 @@
 // (same page, question 7).
 //
 // Work decomposition.  A work unit is one (kv head, tile of query heads of
-// its group); one wave owns one unit over one partition of one sequence and
-// walks every 16-token tile of that partition itself, so its softmax state
-// never has to be merged with another wave's.  A workgroup is up to eight
-// consecutive units of the same (sequence, partition): its waves read the
-// same physical blocks at the same time, so each block's K (and V) rows of
-// neighbouring heads, which are adjacent in memory, are fetched together.
-// On MI355X that keeps the DRAM access stream close to a sequential one
-// (6.9 TB/s for the bare gather, against 5.7 TB/s when each workgroup walks
-// one head on its own).  With a split, each partition leaves a
-// (max, sum, unnormalised output) triple in the workspace and merge_kernel
-// combines them in a fixed order (no atomics, so results are
-// bit-reproducible).
+// its group).  A workgroup is up to eight consecutive units (a unit chunk),
+// one wave each; the waves walk the same token range of the same sequences,
+// so each physical block's K (and V) rows of neighbouring heads, which are
+// adjacent in memory, are fetched together.  On MI355X that keeps the DRAM
+// access stream close to a sequential one (6.9 TB/s for the bare gather,
+// against 5.7 TB/s when each workgroup walks one head on its own).  A wave
+// keeps its own softmax state per sequence piece and never merges it with
+// another wave's.
 //
+// Which token ranges a workgroup takes (the schedule):
+//  * balanced: the 16-token tiles of all sequences, back to back, are dealt
+//    out in equal contiguous shares, one per workgroup of a unit chunk, so
+//    every workgroup moves the same number of bytes whatever the length mix.
+//    Each workgroup works the per-sequence tile offsets out itself from
+//    seq_lens (a prefix sum in LDS), so the host never needs the lengths.
+//  * fixed: one workgroup per fixed-size token partition of one sequence
+//    (or per sequence when unsplit).
+// A sequence that ends up in several pieces leaves one (max, sum,
+// unnormalised output) triple per piece and query head in the workspace;
+// merge_kernel combines them in piece order (no atomics, so results are
+// bit-reproducible).
+
 // Every K/V load reads whole token rows (16 lanes x 16 bytes for a 256-byte
 // row), so a load instruction covers complete 128-byte lines.
 //
@@ -113,26 +122,109 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// What one wave works on: its unit, sequence, partition and token range.
+// One piece of work of a wave: tokens [t_lo, t_hi) of sequence b.
 struct Work {
-  int kvh, htile, b, part, L, t_lo, t_hi, n_tiles;
+  int b, L, t_lo, t_hi, n_tiles;
 };
 
-// false when the wave has nothing to do (unit past the end, or a partition
-// that starts beyond the sequence: its triple is never read).
-__device__ __forceinline__ bool wave_work(const DecodeParams& p, Work& wk) {
-  const int unit = blockIdx.x * p.waves + (threadIdx.x >> 6);
-  if (unit >= p.units) return false;
-  wk.kvh = unit / p.head_tiles;
-  wk.htile = unit - wk.kvh * p.head_tiles;
-  wk.b = blockIdx.z;
-  wk.part = blockIdx.y;
-  wk.L = clamp_len(p, wk.b);
-  wk.t_lo = wk.part * p.part_tokens;
-  if (wk.part > 0 && wk.t_lo >= wk.L) return false;
-  wk.t_hi = min(wk.L, wk.t_lo + p.part_tokens);
-  wk.n_tiles = wk.t_hi > wk.t_lo ? (wk.t_hi - wk.t_lo + kTile - 1) / kTile : 0;
-  return true;
+// Owner (workgroup index within a unit chunk) of tile t when T tiles are
+// dealt to NW workgroups as [floor(w T / NW), floor((w + 1) T / NW)).
+__device__ __forceinline__ int tile_owner(int t, int T, int NW) {
+  return (int)(((int64_t)(t + 1) * NW - 1) / T);
+}
+
+// Balanced schedule: s_pref[b] = tiles of sequences 0..b-1 (b = 0..B), by a
+// workgroup-wide prefix sum; every thread of the workgroup must call it.
+// Returns the total tile count.
+__device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, int* s_wtot) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  if (threadIdx.x == 0) s_pref[0] = 0;
+  int carry = 0;
+  for (int base = 0; base < p.B; base += blockDim.x) {
+    const int b = base + threadIdx.x;
+    int x = b < p.B ? (clamp_len(p, b) + kTile - 1) / kTile : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wtot[w] = x;
+    __syncthreads();
+    int before = carry, total = 0;
+    for (int k = 0; k < nw; ++k) {
+      const int t = s_wtot[k];
+      if (k < w) before += t;
+      total += t;
+    }
+    if (b < p.B) s_pref[b + 1] = before + x;
+    carry += total;
+    __syncthreads();
+  }
+  __syncthreads();
+  return carry;
+}
+
+// Calls f(work, slot) for every piece this wave owns, in order: slot < 0
+// means the piece is the whole sequence (write the output), else the
+// triple slot of the piece.  Every thread of the workgroup must call it
+// (the balanced schedule synchronises the workgroup once at the start);
+// has_unit is false for waves past the last unit.
+template <class F>
+__device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pref, int* s_wtot,
+                                               bool has_unit, F&& f) {
+  if (p.sched == kSchedBalanced) {
+    const int T = tile_prefix(p, s_pref, s_wtot);
+    // never more shares than tiles: then no share is empty, and the owners
+    // of one sequence's tiles are consecutive workgroups (piece k of a
+    // sequence is processed by workgroup first + k)
+    const int NW = min(p.nwc, T);
+    const int wi = blockIdx.y;
+    if (!has_unit || wi >= NW) return;
+    const int tb = (int)((int64_t)wi * T / NW);
+    const int te = (int)((int64_t)(wi + 1) * T / NW);
+    // first sequence whose tiles reach past tb
+    int lo = 0, hi = p.B;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid + 1] > tb) hi = mid;
+      else lo = mid + 1;
+    }
+    for (int b = lo; b < p.B; ++b) {
+      const int sb = s_pref[b], se = s_pref[b + 1];
+      if (sb >= te) break;
+      if (se == sb) continue;  // empty: the merge kernel writes its zeros
+      const int first = tile_owner(sb, T, NW);
+      const int pieces = tile_owner(se - 1, T, NW) - first + 1;
+      const int a = max(tb, sb) - sb;
+      const int e = min(te, se) - sb;
+      if (a == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
+        p.ws_meta[2 * b] = first + b;
+        p.ws_meta[2 * b + 1] = pieces;
+      }
+      Work wk;
+      wk.b = b;
+      wk.L = clamp_len(p, b);
+      wk.t_lo = a * kTile;
+      wk.t_hi = min(e * kTile, wk.L);
+      wk.n_tiles = e - a;
+      // slots first + b .. first + b + pieces - 1 belong to sequence b:
+      // first_wg(b) + b grows by at least pieces(b) from b to b + 1
+      f(wk, pieces > 1 ? first + b + (wi - first) : -1);
+    }
+  } else {
+    if (!has_unit) return;
+    Work wk;
+    wk.b = blockIdx.z;
+    const int part = blockIdx.y;
+    wk.L = clamp_len(p, wk.b);
+    wk.t_lo = part * p.part_tokens;
+    if (part > 0 && wk.t_lo >= wk.L) return;  // its triple is never read
+    wk.t_hi = min(wk.L, wk.t_lo + p.part_tokens);
+    wk.n_tiles = wk.t_hi > wk.t_lo ? (wk.t_hi - wk.t_lo + kTile - 1) / kTile : 0;
+    f(wk, p.split && wk.L > p.part_tokens ? wk.b * p.num_parts + part : -1);
+  }
 }
 
 // Physical block ids of tiles chunk*64 .. chunk*64+63 of the wave's range:
@@ -267,9 +359,9 @@ __device__ __forceinline__ void run_tiles_lds(const DecodeParams& p, const Work&
   }
 }
 
-// Triple slot of (sequence, query head, partition).
-__device__ __forceinline__ int64_t triple_index(const DecodeParams& p, int b, int h, int part) {
-  return ((int64_t)b * p.Hq + h) * p.num_parts + part;
+// Workspace index of the triple of (slot, query head).
+__device__ __forceinline__ int64_t triple_index(const DecodeParams& p, int slot, int h) {
+  return (int64_t)slot * p.Hq + h;
 }
 
 // ============================================================================
@@ -299,36 +391,24 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
   // in-flight tile's LDS writes from the current tile's reads
   __shared__ i32x4 kt0[kMaxWaves][SLOTS];
   __shared__ i32x4 kt1[kMaxWaves][SLOTS];
+  __shared__ int s_pref[kBalancedMaxBatch + 1];
+  __shared__ int s_wtot[kMaxWaves];
 
-  Work wk;
-  if (!wave_work(p, wk)) return;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int gh0 = wk.htile * 16;
+  const int unit = blockIdx.x * p.waves + w;
+  const bool has_unit = unit < p.units;
+  const int kvh = unit / p.head_tiles;
+  const int gh0 = (unit - kvh * p.head_tiles) * 16;
   const int nh = min(16, p.G - gh0);
-  const int head0 = wk.kvh * p.G + gh0;
-
-  // Query group as the B operand of the score MFMAs: lane (n, g) holds head
-  // n, 8 dims per MFMA: those of 16-byte K chunk 4r + g (16-bit K: MFMA r;
-  // fp8 K: the low / high half of that chunk for MFMAs 2r, 2r + 1).
-  i32x4 qop[NJQ];
-  {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)wk.b * p.q_sb +
-                           (int64_t)(head0 + min(n, nh - 1)) * p.q_sh;
-#pragma unroll
-    for (int j = 0; j < NJQ; ++j) {
-      const int d0 = kFP8 ? ((j >> 1) * 64 + g * 16 + (j & 1) * 8) : (j * 32 + g * 8);
-      const i32x4 v = *reinterpret_cast<const i32x4*>(qrow + d0);
-      qop[j] = n < nh ? v : i32x4{0, 0, 0, 0};
-    }
-  }
+  const int head0 = kvh * p.G + gh0;
 
   const int64_t rs = (int64_t)p.Hkv * RB;  // bytes between tokens
   const int64_t blk_bytes = rs * p.bs;
-  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)wk.kvh * RB;
-  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)wk.kvh * RB;
+  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * RB;
+  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * RB;
   // K to LDS: instruction j, lane l loads row tt = j*TPI + l/LR, chunk
   // (l % LR) ^ swz(tt), landing in slot tt*LR + l%LR; so slot tt*LR + s
   // holds chunk s ^ swz(tt) of row tt.
@@ -352,147 +432,177 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
     Bytes<VBYTES> v[4];
   };
 
-  int ids = 0;
-  auto load_tile = [&](int i, i32x4* kt, Regs& r) {
-    const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
-    const char* kb = kbase + tb;
-    const char* vb = vbase + tb;
+  for_each_piece(p, s_pref, s_wtot, has_unit, [&](const Work& wk, int slot) {
+    // Query group as the B operand of the score MFMAs: lane (n, g) holds
+    // head n, 8 dims per MFMA: those of 16-byte K chunk 4r + g (16-bit K:
+    // MFMA r; fp8 K: the low / high half of that chunk for MFMAs 2r, 2r + 1).
+    i32x4 qop[NJQ];
+    {
+      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)wk.b * p.q_sb +
+                             (int64_t)(head0 + min(n, nh - 1)) * p.q_sh;
 #pragma unroll
-    for (int j = 0; j < NK; ++j)
-      load_lds16(kb + kdma[j], kt + j * 64);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r.v[q] = load_bytes<VBYTES>(vb, voff[q]);
-  };
-
-  float m = kMaxFloor;
-  float l = 0.f;
-  f32x4 acc[NJV];
-#pragma unroll
-  for (int j = 0; j < NJV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // K operand chunks of the tile in LDS
-  i32x4 kreg[NR];
-  auto fetch_tile = [&](const i32x4* kt) {
-#pragma unroll
-    for (int rr = 0; rr < NR; ++rr) kreg[rr] = kt[kslot[rr]];
-  };
-
-  auto compute_tile = [&](int i, Regs& r) {
-    const int t0 = wk.t_lo + kTile * i;
-    // scores: D[token 4g+q][head n]
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int rr = 0; rr < NR; ++rr) {
-      const i32x4 kc = kreg[rr];
-      if constexpr (kFP8) {
-        const i32x2 c0 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[0]) : fp8x4_to_f16x4((uint32_t)kc[0]);
-        const i32x2 c1 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[1]) : fp8x4_to_f16x4((uint32_t)kc[1]);
-        const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[2]) : fp8x4_to_f16x4((uint32_t)kc[2]);
-        const i32x2 c3 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[3]) : fp8x4_to_f16x4((uint32_t)kc[3]);
-        s = mfma_k32<kBF16>(i32x4{c0[0], c0[1], c1[0], c1[1]}, qop[2 * rr], s);
-        s = mfma_k32<kBF16>(i32x4{c2[0], c2[1], c3[0], c3[1]}, qop[2 * rr + 1], s);
-      } else {
-        s = mfma_k32<kBF16>(kc, qop[rr], s);
+      for (int j = 0; j < NJQ; ++j) {
+        const int d0 = kFP8 ? ((j >> 1) * 64 + g * 16 + (j & 1) * 8) : (j * 32 + g * 8);
+        const i32x4 v = *reinterpret_cast<const i32x4*>(qrow + d0);
+        qop[j] = n < nh ? v : i32x4{0, 0, 0, 0};
       }
     }
-    float sv[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      sv[q] = (t0 + 4 * g + q < wk.t_hi) ? s[q] * p.qk_scale_log2 : -INFINITY;
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    const float p0 = fast_exp2(sv[0] - m_new), p1 = fast_exp2(sv[1] - m_new);
-    const float p2 = fast_exp2(sv[2] - m_new), p3 = fast_exp2(sv[3] - m_new);
-    const uint32_t pw0 = kBF16 ? pack_bf16(p0, p1) : pack_f16(p0, p1);
-    const uint32_t pw1 = kBF16 ? pack_bf16(p2, p3) : pack_f16(p2, p3);
-    // the denominator sums the same rounded weights the product uses
-    const float ps = kBF16 ? (bf16_lo(pw0) + bf16_hi(pw0)) + (bf16_lo(pw1) + bf16_hi(pw1))
-                           : (f16_lo(pw0) + f16_hi(pw0)) + (f16_lo(pw1) + f16_hi(pw1));
-    l = l * alpha + ps;
-    m = m_new;
-    const i32x2 pop = {(int)pw0, (int)pw1};
 
-    // V rows as 16-bit words: vw[q][k] holds elements 2k, 2k+1 of token 4g+q.
-    // Tokens past the end of the sequence may hold anything (NaN poison):
-    // their rows are replaced by zeros (a select, not a branch, so the loads
-    // still in flight are not waited for) before the P x V product.
-    uint32_t vw[4][VW];
+    int ids = 0;
+    auto load_tile = [&](int i, i32x4* kt, Regs& r) {
+      const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
+      const char* kb = kbase + tb;
+      const char* vb = vbase + tb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool ok = t0 + 4 * g + q < wk.t_hi;
-      if constexpr (kFP8) {
+      for (int j = 0; j < NK; ++j) load_lds16(kb + kdma[j], kt + j * 64);
 #pragma unroll
-        for (int k = 0; k < VW / 2; ++k) {
-          const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4(r.v[q].w(k)) : fp8x4_to_f16x4(r.v[q].w(k));
-          vw[q][2 * k] = ok ? (uint32_t)c2[0] : 0u;
-          vw[q][2 * k + 1] = ok ? (uint32_t)c2[1] : 0u;
+      for (int q = 0; q < 4; ++q) r.v[q] = load_bytes<VBYTES>(vb, voff[q]);
+    };
+
+    float m = kMaxFloor;
+    float l = 0.f;
+    f32x4 acc[NJV];
+#pragma unroll
+    for (int j = 0; j < NJV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // K operand chunks of the tile in LDS
+    i32x4 kreg[NR];
+    auto fetch_tile = [&](const i32x4* kt) {
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) kreg[rr] = kt[kslot[rr]];
+    };
+
+    auto compute_tile = [&](int i, Regs& r) {
+      const int t0 = wk.t_lo + kTile * i;
+      // scores: D[token 4g+q][head n]
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rr = 0; rr < NR; ++rr) {
+        const i32x4 kc = kreg[rr];
+        if constexpr (kFP8) {
+          const i32x2 c0 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[0]) : fp8x4_to_f16x4((uint32_t)kc[0]);
+          const i32x2 c1 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[1]) : fp8x4_to_f16x4((uint32_t)kc[1]);
+          const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[2]) : fp8x4_to_f16x4((uint32_t)kc[2]);
+          const i32x2 c3 = kBF16 ? fp8x4_to_bf16x4((uint32_t)kc[3]) : fp8x4_to_f16x4((uint32_t)kc[3]);
+          s = mfma_k32<kBF16>(i32x4{c0[0], c0[1], c1[0], c1[1]}, qop[2 * rr], s);
+          s = mfma_k32<kBF16>(i32x4{c2[0], c2[1], c3[0], c3[1]}, qop[2 * rr + 1], s);
+        } else {
+          s = mfma_k32<kBF16>(kc, qop[rr], s);
         }
-      } else {
+      }
+      float sv[4];
 #pragma unroll
-        for (int k = 0; k < VW; ++k) vw[q][k] = ok ? r.v[q].w(k) : 0u;
+      for (int q = 0; q < 4; ++q)
+        sv[q] = (t0 + 4 * g + q < wk.t_hi) ? s[q] * p.qk_scale_log2 : -INFINITY;
+      float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      const float p0 = fast_exp2(sv[0] - m_new), p1 = fast_exp2(sv[1] - m_new);
+      const float p2 = fast_exp2(sv[2] - m_new), p3 = fast_exp2(sv[3] - m_new);
+      // P as the B operand of the P x V MFMAs.  fp16 (11-bit significand)
+      // is precise enough on its own; bf16 (8 bits) would put errors of
+      // 2^-9 |v| on outputs whose terms nearly cancel, so there P goes in
+      // as hi + lo, two bf16 values whose sum carries 16 bits, and the
+      // product runs twice.  The denominator sums the same rounded weights
+      // the product uses.
+      const uint32_t pw0 = kBF16 ? pack_bf16(p0, p1) : pack_f16(p0, p1);
+      const uint32_t pw1 = kBF16 ? pack_bf16(p2, p3) : pack_f16(p2, p3);
+      float ps;
+      i32x2 pop_lo = {0, 0};
+      if constexpr (kBF16) {
+        const float h0 = bf16_lo(pw0), h1 = bf16_hi(pw0), h2 = bf16_lo(pw1), h3 = bf16_hi(pw1);
+        const uint32_t lw0 = pack_bf16(p0 - h0, p1 - h1);
+        const uint32_t lw1 = pack_bf16(p2 - h2, p3 - h3);
+        ps = ((h0 + bf16_lo(lw0)) + (h1 + bf16_hi(lw0))) + ((h2 + bf16_lo(lw1)) + (h3 + bf16_hi(lw1)));
+        pop_lo = i32x2{(int)lw0, (int)lw1};
+      } else {
+        ps = (f16_lo(pw0) + f16_hi(pw0)) + (f16_lo(pw1) + f16_hi(pw1));
+      }
+      l = l * alpha + ps;
+      m = m_new;
+      const i32x2 pop = {(int)pw0, (int)pw1};
+
+      // V rows as 16-bit words: vw[q][k] holds elements 2k, 2k+1 of token
+      // 4g+q.  Tokens past the end of the sequence may hold anything (NaN
+      // poison): their rows are replaced by zeros (a select, not a branch,
+      // so the loads still in flight are not waited for) before P x V.
+      uint32_t vw[4][VW];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = t0 + 4 * g + q < wk.t_hi;
+        if constexpr (kFP8) {
+#pragma unroll
+          for (int k = 0; k < VW / 2; ++k) {
+            const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4(r.v[q].w(k)) : fp8x4_to_f16x4(r.v[q].w(k));
+            vw[q][2 * k] = ok ? (uint32_t)c2[0] : 0u;
+            vw[q][2 * k + 1] = ok ? (uint32_t)c2[1] : 0u;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < VW; ++k) vw[q][k] = ok ? r.v[q].w(k) : 0u;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJV; ++j) {
+        const int k = j >> 1;
+        uint32_t a0, a1;
+        if (j & 1) {
+          a0 = pack_hi_halves(vw[0][k], vw[1][k]);
+          a1 = pack_hi_halves(vw[2][k], vw[3][k]);
+        } else {
+          a0 = pack_lo_halves(vw[0][k], vw[1][k]);
+          a1 = pack_lo_halves(vw[2][k], vw[3][k]);
+        }
+        acc[j] = acc[j] * alpha;
+        acc[j] = mfma_k16<kBF16>(i32x2{(int)a0, (int)a1}, pop, acc[j]);
+        if constexpr (kBF16) acc[j] = mfma_k16<kBF16>(i32x2{(int)a0, (int)a1}, pop_lo, acc[j]);
+      }
+    };
+
+    // two K tiles in LDS and two V register sets in ping-pong: the next
+    // tile's loads are in flight while the current tile is computed
+    {
+      Regs r0, r1;
+      run_tiles_lds(
+          p, wk, ids, [&](int i) { load_tile(i, kt0[w], r0); },
+          [&](int i) { load_tile(i, kt1[w], r1); }, [&]() { fetch_tile(kt0[w]); },
+          [&]() { fetch_tile(kt1[w]); }, [&](int i) { compute_tile(i, r0); },
+          [&](int i) { compute_tile(i, r1); });
+    }
+
+    // lane groups hold partial sums over different tokens
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (n >= nh) return;
+    const int h = head0 + n;
+    // lane (n, g) holds out[h][(4g+i)*NJV + j] in acc[j][i]
+    if (slot >= 0) {
+      const int64_t ti = triple_index(p, slot, h);
+      if (g == 0) {
+        p.ws_ml[2 * ti] = m;
+        p.ws_ml[2 * ti + 1] = l;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[NJV];
+#pragma unroll
+        for (int j = 0; j < NJV; ++j) x[j] = acc[j][i];
+        store_f32_vec<NJV>(p.ws_acc + ti * D + (4 * g + i) * NJV, x);
+      }
+    } else {
+      const float sc = l > 0.f ? p.v_scale / l : 0.f;
+      const int64_t ob = (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x[NJV];
+#pragma unroll
+        for (int j = 0; j < NJV; ++j) x[j] = acc[j][i] * sc;
+        store_out_vec<QK, NJV>(p.out, ob + (4 * g + i) * NJV, x);
       }
     }
-#pragma unroll
-    for (int j = 0; j < NJV; ++j) {
-      const int k = j >> 1;
-      uint32_t a0, a1;
-      if (j & 1) {
-        a0 = pack_hi_halves(vw[0][k], vw[1][k]);
-        a1 = pack_hi_halves(vw[2][k], vw[3][k]);
-      } else {
-        a0 = pack_lo_halves(vw[0][k], vw[1][k]);
-        a1 = pack_lo_halves(vw[2][k], vw[3][k]);
-      }
-      acc[j] = acc[j] * alpha;
-      acc[j] = mfma_k16<kBF16>(i32x2{(int)a0, (int)a1}, pop, acc[j]);
-    }
-  };
-
-  // two K tiles in LDS and two V register sets in ping-pong: the next
-  // tile's loads are in flight while the current tile is computed
-  {
-    Regs r0, r1;
-    run_tiles_lds(
-        p, wk, ids, [&](int i) { load_tile(i, kt0[w], r0); },
-        [&](int i) { load_tile(i, kt1[w], r1); }, [&]() { fetch_tile(kt0[w]); },
-        [&]() { fetch_tile(kt1[w]); }, [&](int i) { compute_tile(i, r0); },
-        [&](int i) { compute_tile(i, r1); });
-  }
-
-  // lane groups hold partial sums over different tokens
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (n >= nh) return;
-  const int h = head0 + n;
-  // lane (n, g) holds out[h][(4g+i)*NJV + j] in acc[j][i]
-  const bool triple = p.split && wk.L > p.part_tokens;
-  if (triple) {
-    const int64_t ti = triple_index(p, wk.b, h, wk.part);
-    if (g == 0) {
-      p.ws_ml[2 * ti] = m;
-      p.ws_ml[2 * ti + 1] = l;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x[NJV];
-#pragma unroll
-      for (int j = 0; j < NJV; ++j) x[j] = acc[j][i];
-      store_f32_vec<NJV>(p.ws_acc + ti * D + (4 * g + i) * NJV, x);
-    }
-  } else {
-    const float sc = l > 0.f ? p.v_scale / l : 0.f;
-    const int64_t ob = (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x[NJV];
-#pragma unroll
-      for (int j = 0; j < NJV; ++j) x[j] = acc[j][i] * sc;
-      store_out_vec<QK, NJV>(p.out, ob + (4 * g + i) * NJV, x);
-    }
-  }
+  });
 }
 
 // ============================================================================
@@ -511,56 +621,23 @@ __global__ __launch_bounds__(kMaxThreads) void decode_valu_kernel(const DecodePa
   static_assert(!kDot2 || QK == KVK, "16-bit KV needs a query of the same type");
   static_assert(VEC % 4 == 0, "shape");
 
-  Work wk;
-  if (!wave_work(p, wk)) return;
+  __shared__ int s_pref[kBalancedMaxBatch + 1];
+  __shared__ int s_wtot[kMaxWaves];
+
   const int lane = threadIdx.x & 63;
   const int r = lane / LPT;          // token slot of this lane in a load
   const int c = lane - r * LPT;      // 16-byte chunk of the row
-  const int gh0 = wk.htile * GT;
+  const int unit = blockIdx.x * p.waves + (threadIdx.x >> 6);
+  const bool has_unit = unit < p.units;
+  const int kvh = unit / p.head_tiles;
+  const int gh0 = (unit - kvh * p.head_tiles) * GT;
   const int nh = min(GT, p.G - gh0);
-  const int head0 = wk.kvh * p.G + gh0;
-
-  // query chunk of each head: packed 16-bit words for v_dot2, else fp32
-  // pre-multiplied by the score scale
-  uint32_t qw[GT][kDot2 ? QE / 2 : 1];
-  float qf[GT][kDot2 ? 1 : QE];
-#pragma unroll
-  for (int gh = 0; gh < GT; ++gh) {
-    const int hq = head0 + min(gh, nh - 1);
-    const int64_t qo = (int64_t)wk.b * p.q_sb + (int64_t)hq * p.q_sh + c * QE;
-    if constexpr (kDot2) {
-      const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + qo);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qw[gh][k] = (uint32_t)v[k];
-    } else if constexpr (QK == K_F32) {
-#pragma unroll
-      for (int k = 0; k < QE; k += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + qo + k);
-        qf[gh][k] = v[0] * p.qk_scale_log2;
-        qf[gh][k + 1] = v[1] * p.qk_scale_log2;
-        qf[gh][k + 2] = v[2] * p.qk_scale_log2;
-        qf[gh][k + 3] = v[3] * p.qk_scale_log2;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < QE; k += 8) {
-        const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + qo + k);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t wd = (uint32_t)v[e];
-          const float lo = QK == K_BF16 ? bf16_lo(wd) : f16_lo(wd);
-          const float hi = QK == K_BF16 ? bf16_hi(wd) : f16_hi(wd);
-          qf[gh][k + 2 * e] = lo * p.qk_scale_log2;
-          qf[gh][k + 2 * e + 1] = hi * p.qk_scale_log2;
-        }
-      }
-    }
-  }
+  const int head0 = kvh * p.G + gh0;
 
   const int64_t rs = (int64_t)p.Hkv * D * ESZ;
   const int64_t blk_bytes = rs * p.bs;
-  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)wk.kvh * D * ESZ;
-  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)wk.kvh * D * ESZ;
+  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
+  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
   uint32_t off[NL];
 #pragma unroll
   for (int li = 0; li < NL; ++li) off[li] = (uint32_t)((li * TPL + r) * rs + c * 16);
@@ -569,197 +646,289 @@ __global__ __launch_bounds__(kMaxThreads) void decode_valu_kernel(const DecodePa
     Bytes<16> k[NL];
     Bytes<16> v[NL];
   };
-  int ids = 0;
-  auto load_tile = [&](int i, Regs& rg) {
-    const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
-#pragma unroll
-    for (int li = 0; li < NL; ++li) rg.k[li] = load_bytes<16>(kbase + tb, off[li]);
-#pragma unroll
-    for (int li = 0; li < NL; ++li) rg.v[li] = load_bytes<16>(vbase + tb, off[li]);
-  };
 
-  float m[GT], lsum[GT], acc[GT][VEC];
+  for_each_piece(p, s_pref, s_wtot, has_unit, [&](const Work& wk, int slot) {
+    // query chunk of each head: packed 16-bit words for v_dot2, else fp32
+    // pre-multiplied by the score scale
+    uint32_t qw[GT][kDot2 ? QE / 2 : 1];
+    float qf[GT][kDot2 ? 1 : QE];
 #pragma unroll
-  for (int gh = 0; gh < GT; ++gh) {
-    m[gh] = kMaxFloor;
-    lsum[gh] = 0.f;
+    for (int gh = 0; gh < GT; ++gh) {
+      const int hq = head0 + min(gh, nh - 1);
+      const int64_t qo = (int64_t)wk.b * p.q_sb + (int64_t)hq * p.q_sh + c * QE;
+      if constexpr (kDot2) {
+        const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + qo);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[gh][e] = 0.f;
-  }
-
-  auto compute_tile = [&](int i, Regs& rg) {
-    const int t0 = wk.t_lo + kTile * i;
-    // tokens past the end of the sequence may hold anything (NaN poison):
-    // their scores become -inf and their V rows zeros, by selects (not
-    // branches, so the loads still in flight are not waited for)
-    bool valid[NL];
+        for (int k = 0; k < 4; ++k) qw[gh][k] = (uint32_t)v[k];
+      } else if constexpr (QK == K_F32) {
 #pragma unroll
-    for (int li = 0; li < NL; ++li) valid[li] = t0 + li * TPL + r < wk.t_hi;
-    // scores (log2 units) of the NL tokens this row holds
-    float sc[GT][NL];
+        for (int k = 0; k < QE; k += 4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.q) + qo + k);
+          qf[gh][k] = v[0] * p.qk_scale_log2;
+          qf[gh][k + 1] = v[1] * p.qk_scale_log2;
+          qf[gh][k + 2] = v[2] * p.qk_scale_log2;
+          qf[gh][k + 3] = v[3] * p.qk_scale_log2;
+        }
+      } else {
 #pragma unroll
-    for (int li = 0; li < NL; ++li) {
+        for (int k = 0; k < QE; k += 8) {
+          const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(p.q) + qo + k);
 #pragma unroll
-      for (int gh = 0; gh < GT; ++gh) {
-        float d = 0.f;
-        if constexpr (KVK == K_F16) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, rg.k[li].w(k)),
-                                       __builtin_bit_cast(f16x2, qw[gh][k]), d, false);
-        } else if constexpr (KVK == K_BF16) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rg.k[li].w(k)),
-                                                __builtin_bit_cast(bf16x2, qw[gh][k]), d, false);
-        } else if constexpr (KVK == K_F32) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) d += __builtin_bit_cast(float, rg.k[li].w(k)) * qf[gh][k];
-        } else {  // fp8: 16 elements
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const f32x4 kv = fp8x4_to_f32x4(rg.k[li].w(k));
-            d += kv[0] * qf[gh][4 * k] + kv[1] * qf[gh][4 * k + 1] +
-                 kv[2] * qf[gh][4 * k + 2] + kv[3] * qf[gh][4 * k + 3];
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wd = (uint32_t)v[e];
+            const float lo = QK == K_BF16 ? bf16_lo(wd) : f16_lo(wd);
+            const float hi = QK == K_BF16 ? bf16_hi(wd) : f16_hi(wd);
+            qf[gh][k + 2 * e] = lo * p.qk_scale_log2;
+            qf[gh][k + 2 * e + 1] = hi * p.qk_scale_log2;
           }
         }
-        d = group_sum<LPT>(d);
-        if constexpr (kDot2) d *= p.qk_scale_log2;
-        sc[gh][li] = valid[li] ? d : -INFINITY;
       }
     }
-    // V rows to fp32
-    float vf[NL][VEC];
+
+    int ids = 0;
+    auto load_tile = [&](int i, Regs& rg) {
+      const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
 #pragma unroll
-    for (int li = 0; li < NL; ++li) {
+      for (int li = 0; li < NL; ++li) rg.k[li] = load_bytes<16>(kbase + tb, off[li]);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t wd = valid[li] ? rg.v[li].w(k) : 0u;
-        if constexpr (KVK == K_F32) {
-          vf[li][k] = __builtin_bit_cast(float, wd);
-        } else if constexpr (KVK == K_F16) {
-          vf[li][2 * k] = f16_lo(wd);
-          vf[li][2 * k + 1] = f16_hi(wd);
-        } else if constexpr (KVK == K_BF16) {
-          vf[li][2 * k] = bf16_lo(wd);
-          vf[li][2 * k + 1] = bf16_hi(wd);
-        } else {
-          const f32x4 x = fp8x4_to_f32x4(wd);
-          vf[li][4 * k] = x[0];
-          vf[li][4 * k + 1] = x[1];
-          vf[li][4 * k + 2] = x[2];
-          vf[li][4 * k + 3] = x[3];
-        }
-      }
-    }
+      for (int li = 0; li < NL; ++li) rg.v[li] = load_bytes<16>(vbase + tb, off[li]);
+    };
+
+    float m[GT], lsum[GT], acc[GT][VEC];
 #pragma unroll
     for (int gh = 0; gh < GT; ++gh) {
-      float mx = sc[gh][0];
+      m[gh] = kMaxFloor;
+      lsum[gh] = 0.f;
 #pragma unroll
-      for (int li = 1; li < NL; ++li) mx = fmaxf(mx, sc[gh][li]);
-      const float m_new = fmaxf(m[gh], mx);
-      const float alpha = fast_exp2(m[gh] - m_new);
-      float pr[NL];
-      float ps = 0.f;
+      for (int e = 0; e < VEC; ++e) acc[gh][e] = 0.f;
+    }
+
+    auto compute_tile = [&](int i, Regs& rg) {
+      const int t0 = wk.t_lo + kTile * i;
+      // tokens past the end of the sequence may hold anything (NaN poison):
+      // their scores become -inf and their V rows zeros, by selects (not
+      // branches, so the loads still in flight are not waited for)
+      bool valid[NL];
+#pragma unroll
+      for (int li = 0; li < NL; ++li) valid[li] = t0 + li * TPL + r < wk.t_hi;
+      // scores (log2 units) of the NL tokens this row holds
+      float sc[GT][NL];
 #pragma unroll
       for (int li = 0; li < NL; ++li) {
-        pr[li] = fast_exp2(sc[gh][li] - m_new);
-        ps += pr[li];
+#pragma unroll
+        for (int gh = 0; gh < GT; ++gh) {
+          float d = 0.f;
+          if constexpr (KVK == K_F16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              d = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, rg.k[li].w(k)),
+                                         __builtin_bit_cast(f16x2, qw[gh][k]), d, false);
+          } else if constexpr (KVK == K_BF16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+              d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, rg.k[li].w(k)),
+                                                  __builtin_bit_cast(bf16x2, qw[gh][k]), d, false);
+          } else if constexpr (KVK == K_F32) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) d += __builtin_bit_cast(float, rg.k[li].w(k)) * qf[gh][k];
+          } else {  // fp8: 16 elements
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f32x4 kv = fp8x4_to_f32x4(rg.k[li].w(k));
+              d += kv[0] * qf[gh][4 * k] + kv[1] * qf[gh][4 * k + 1] +
+                   kv[2] * qf[gh][4 * k + 2] + kv[3] * qf[gh][4 * k + 3];
+            }
+          }
+          d = group_sum<LPT>(d);
+          if constexpr (kDot2) d *= p.qk_scale_log2;
+          sc[gh][li] = valid[li] ? d : -INFINITY;
+        }
       }
-      lsum[gh] = lsum[gh] * alpha + ps;
-      m[gh] = m_new;
+      // V rows to fp32
+      float vf[NL][VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float a = acc[gh][e] * alpha;
+      for (int li = 0; li < NL; ++li) {
 #pragma unroll
-        for (int li = 0; li < NL; ++li) a += pr[li] * vf[li][e];
-        acc[gh][e] = a;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t wd = valid[li] ? rg.v[li].w(k) : 0u;
+          if constexpr (KVK == K_F32) {
+            vf[li][k] = __builtin_bit_cast(float, wd);
+          } else if constexpr (KVK == K_F16) {
+            vf[li][2 * k] = f16_lo(wd);
+            vf[li][2 * k + 1] = f16_hi(wd);
+          } else if constexpr (KVK == K_BF16) {
+            vf[li][2 * k] = bf16_lo(wd);
+            vf[li][2 * k + 1] = bf16_hi(wd);
+          } else {
+            const f32x4 x = fp8x4_to_f32x4(wd);
+            vf[li][4 * k] = x[0];
+            vf[li][4 * k + 1] = x[1];
+            vf[li][4 * k + 2] = x[2];
+            vf[li][4 * k + 3] = x[3];
+          }
+        }
+      }
+#pragma unroll
+      for (int gh = 0; gh < GT; ++gh) {
+        float mx = sc[gh][0];
+#pragma unroll
+        for (int li = 1; li < NL; ++li) mx = fmaxf(mx, sc[gh][li]);
+        const float m_new = fmaxf(m[gh], mx);
+        const float alpha = fast_exp2(m[gh] - m_new);
+        float pr[NL];
+        float ps = 0.f;
+#pragma unroll
+        for (int li = 0; li < NL; ++li) {
+          pr[li] = fast_exp2(sc[gh][li] - m_new);
+          ps += pr[li];
+        }
+        lsum[gh] = lsum[gh] * alpha + ps;
+        m[gh] = m_new;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          float a = acc[gh][e] * alpha;
+#pragma unroll
+          for (int li = 0; li < NL; ++li) a += pr[li] * vf[li][e];
+          acc[gh][e] = a;
+        }
+      }
+    };
+
+    // two register sets in ping-pong: the next tile's loads are in flight
+    // while the current tile is computed
+    {
+      Regs r0, r1;
+      run_tiles(
+          p, wk, ids, [&](int i) { load_tile(i, r0); }, [&](int i) { load_tile(i, r1); },
+          [&](int i) { compute_tile(i, r0); }, [&](int i) { compute_tile(i, r1); });
+    }
+
+    // rows of the wave hold disjoint tokens: merge their states (lanes with
+    // the same chunk c sit LPT, 2*LPT, ... lanes apart)
+#pragma unroll
+    for (int step = LPT; step < 64; step <<= 1) {
+#pragma unroll
+      for (int gh = 0; gh < GT; ++gh) {
+        const float mo = __shfl_xor(m[gh], step);
+        const float lo = __shfl_xor(lsum[gh], step);
+        const float mm = fmaxf(m[gh], mo);
+        const float s1 = fast_exp2(m[gh] - mm);
+        const float s2 = fast_exp2(mo - mm);
+        lsum[gh] = lsum[gh] * s1 + lo * s2;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float ao = __shfl_xor(acc[gh][e], step);
+          acc[gh][e] = acc[gh][e] * s1 + ao * s2;
+        }
+        m[gh] = mm;
       }
     }
-  };
-
-  // two register sets in ping-pong: the next tile's loads are in flight
-  // while the current tile is computed
-  {
-    Regs r0, r1;
-    run_tiles(
-        p, wk, ids, [&](int i) { load_tile(i, r0); }, [&](int i) { load_tile(i, r1); },
-        [&](int i) { compute_tile(i, r0); }, [&](int i) { compute_tile(i, r1); });
-  }
-
-  // rows of the wave hold disjoint tokens: merge their states (lanes with the
-  // same chunk c sit LPT, 2*LPT, ... lanes apart)
-#pragma unroll
-  for (int step = LPT; step < 64; step <<= 1) {
+    if (r != 0) return;
 #pragma unroll
     for (int gh = 0; gh < GT; ++gh) {
-      const float mo = __shfl_xor(m[gh], step);
-      const float lo = __shfl_xor(lsum[gh], step);
-      const float mm = fmaxf(m[gh], mo);
-      const float s1 = fast_exp2(m[gh] - mm);
-      const float s2 = fast_exp2(mo - mm);
-      lsum[gh] = lsum[gh] * s1 + lo * s2;
+      if (gh >= nh) break;
+      const int h = head0 + gh;
+      if (slot >= 0) {
+        const int64_t ti = triple_index(p, slot, h);
+        if (c == 0) {
+          p.ws_ml[2 * ti] = m[gh];
+          p.ws_ml[2 * ti + 1] = lsum[gh];
+        }
+        store_f32_vec<VEC>(p.ws_acc + ti * D + c * VEC, acc[gh]);
+      } else {
+        const float sc = lsum[gh] > 0.f ? p.v_scale / lsum[gh] : 0.f;
+        float x[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const float ao = __shfl_xor(acc[gh][e], step);
-        acc[gh][e] = acc[gh][e] * s1 + ao * s2;
+        for (int e = 0; e < VEC; ++e) x[e] = acc[gh][e] * sc;
+        store_out_vec<QK, VEC>(p.out, (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh + c * VEC, x);
       }
-      m[gh] = mm;
     }
-  }
-  if (r != 0) return;
-  const bool triple = p.split && wk.L > p.part_tokens;
-#pragma unroll
-  for (int gh = 0; gh < GT; ++gh) {
-    if (gh >= nh) break;
-    const int h = head0 + gh;
-    if (triple) {
-      const int64_t ti = triple_index(p, wk.b, h, wk.part);
-      if (c == 0) {
-        p.ws_ml[2 * ti] = m[gh];
-        p.ws_ml[2 * ti + 1] = lsum[gh];
-      }
-      store_f32_vec<VEC>(p.ws_acc + ti * D + c * VEC, acc[gh]);
-    } else {
-      const float sc = lsum[gh] > 0.f ? p.v_scale / lsum[gh] : 0.f;
-      float x[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[e] = acc[gh][e] * sc;
-      store_out_vec<QK, VEC>(p.out, (int64_t)wk.b * p.o_sb + (int64_t)h * p.o_sh + c * VEC, x);
-    }
-  }
+  });
 }
 
 // ============================================================================
-// Partition merge: out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M),
-// partitions in increasing order.
+// Piece merge: out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) with
+// M = max_p m_p.  One 256-thread workgroup per (query head, sequence): a
+// workgroup-wide max over the pieces, then GROUPS groups of D/4 threads
+// (4 dims each, 16-byte loads) take every GROUPS-th piece, and the group
+// partial sums are added in group order (a fixed order: the result does not
+// depend on timing).  Under the balanced schedule it also writes the zero
+// rows of empty sequences (no piece exists for them).
 // ============================================================================
+constexpr int kMergeThreads = 256;
+
 template <int QK, int D>
-__global__ __launch_bounds__(D) void merge_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams p) {
+  constexpr int TPR = D / 4;                   // threads per piece row
+  constexpr int GROUPS = kMergeThreads / TPR;  // pieces summed side by side
+  __shared__ float s_red[kMergeThreads / 64];
+  __shared__ f32x4 s_num[GROUPS][TPR];
+  __shared__ float s_den[GROUPS];
+
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
   const int L = clamp_len(p, b);
-  if (L <= p.part_tokens) return;  // single partition: written directly
-  const int P = (L + p.part_tokens - 1) / p.part_tokens;
-  const int64_t base = triple_index(p, b, h, 0);
-  const float* ml = p.ws_ml + 2 * base;
-  const float* acc = p.ws_acc + base * D + d;
-  float M = kMaxFloor;
-  for (int q = 0; q < P; ++q) M = fmaxf(M, ml[2 * q]);
-  float num = 0.f, den = 0.f;
-  for (int q = 0; q < P; ++q) {
-    const float sc = fast_exp2(ml[2 * q] - M);
-    den += ml[2 * q + 1] * sc;
-    num += acc[(int64_t)q * D] * sc;
+  const int64_t ob = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
+  int slot0, P;
+  if (p.sched == kSchedBalanced) {
+    if (L == 0) {
+      if (tid < D) store_out<QK>(p.out, ob + tid, 0.f);
+      return;
+    }
+    slot0 = p.ws_meta[2 * b];
+    P = p.ws_meta[2 * b + 1];
+    if (P <= 1) return;  // single piece: written directly
+  } else {
+    if (L <= p.part_tokens) return;  // single partition: written directly
+    slot0 = b * p.num_parts;
+    P = (L + p.part_tokens - 1) / p.part_tokens;
   }
-  const float o = den > 0.f ? num / den * p.v_scale : 0.f;
-  store_out<QK>(p.out, (int64_t)b * p.o_sb + (int64_t)h * p.o_sh + d, o);
+  // triple of piece q: index base + q * Hq
+  const int64_t base = triple_index(p, slot0, h);
+  const int64_t step = p.Hq;
+
+  float M = kMaxFloor;
+  for (int q = tid; q < P; q += kMergeThreads) M = fmaxf(M, p.ws_ml[2 * (base + q * step)]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
+  __syncthreads();
+  M = s_red[0];
+#pragma unroll
+  for (int k = 1; k < kMergeThreads / 64; ++k) M = fmaxf(M, s_red[k]);
+
+  const int grp = tid / TPR;
+  const int c = tid - grp * TPR;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll 4
+  for (int q = grp; q < P; q += GROUPS) {
+    const int64_t ti = base + q * step;
+    const float sc = fast_exp2(p.ws_ml[2 * ti] - M);
+    den += p.ws_ml[2 * ti + 1] * sc;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p.ws_acc + ti * D + 4 * c);
+    num += a * sc;
+  }
+  s_num[grp][c] = num;
+  if (c == 0) s_den[grp] = den;
+  __syncthreads();
+  if (tid >= TPR) return;
+  f32x4 tot = s_num[0][tid];
+  float dtot = s_den[0];
+#pragma unroll
+  for (int k = 1; k < GROUPS; ++k) {
+    tot += s_num[k][tid];
+    dtot += s_den[k];
+  }
+  const float sc = dtot > 0.f ? p.v_scale / dtot : 0.f;
+  float x[4] = {tot[0] * sc, tot[1] * sc, tot[2] * sc, tot[3] * sc};
+  store_out_vec<QK, 4>(p.out, ob + 4 * tid, x);
 }
 
 template <int QK, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<QK, D>), dim3(p.Hq, p.B), dim3(D), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<QK, D>), dim3(p.Hq, p.B), dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -777,7 +946,10 @@ hipError_t launch_valu(const DecodeParams& p, int gt, dim3 grid, dim3 block, hip
 template <int QK, int KVK, int D>
 hipError_t launch_all(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {
   if (p.waves < 1 || p.waves > kMaxWaves) return hipErrorInvalidValue;
-  const dim3 grid((p.units + p.waves - 1) / p.waves, p.num_parts, p.B);
+  if (p.sched == kSchedBalanced && (p.B > kBalancedMaxBatch || p.nwc < 1 || p.nwc > kBalancedWorkgroups))
+    return hipErrorInvalidValue;
+  const int chunks = (p.units + p.waves - 1) / p.waves;
+  const dim3 grid = p.sched == kSchedBalanced ? dim3(chunks, p.nwc, 1) : dim3(chunks, p.num_parts, p.B);
   const dim3 block(p.waves * 64);
   hipError_t e;
   if (v.path == 2) {

@@ -9,6 +9,19 @@ namespace pa {
 
 enum Kind : int { K_F32 = 0, K_F16 = 1, K_BF16 = 2, K_FP8 = 3 };
 
+// Decode schedules.  Fixed: grid (unit chunks, partitions, sequences), one
+// workgroup per fixed-size token partition of one sequence.  Balanced: grid
+// (unit chunks, nwc), the batch's 16-token tiles (all sequences back to
+// back) dealt out in equal contiguous shares, one per workgroup; a share
+// may cover the end of one sequence and the start of the next.
+enum Sched : int { kSchedFixed = 0, kSchedBalanced = 1 };
+
+// Balanced schedule limits: workgroups per unit chunk (the workspace is
+// sized for this many) and the largest batch it takes (the per-sequence
+// tile offsets live in LDS).
+constexpr int kBalancedWorkgroups = 256;
+constexpr int kBalancedMaxBatch = 2048;
+
 // Everything the decode kernels read, resolved on the host.
 struct DecodeParams {
   void* out;              // [B, Hq, D] query dtype
@@ -17,8 +30,9 @@ struct DecodeParams {
   const void* vc;
   const int32_t* tables;  // [B, tab_stride]
   const int32_t* lens;    // [B]
-  float* ws_acc;          // [B, Hq, P, D] partial outputs (split only)
-  float* ws_ml;           // [B, Hq, P, 2] (max, sum) (split only)
+  float* ws_acc;          // [slots, Hq, D] partial outputs (split only)
+  float* ws_ml;           // [slots, Hq, 2] (max, sum) (split only)
+  int32_t* ws_meta;       // [B, 2] (first slot, pieces) (balanced schedule)
   int64_t q_sb, q_sh;     // query strides (elements)
   int64_t o_sb, o_sh;     // output strides
   int64_t tab_stride;     // block-table row stride
@@ -27,9 +41,11 @@ struct DecodeParams {
   int32_t head_tiles;     // ceil(G / tile heads)
   int32_t units;          // Hkv * head_tiles: one wave each per partition
   int32_t waves;          // waves per workgroup (consecutive units)
-  int32_t part_tokens;    // tokens per partition (multiple of 16)
-  int32_t num_parts;      // partitions per sequence in the grid (>= 1)
-  int32_t split;          // 1: write triples and merge afterwards
+  int32_t sched;          // kSchedFixed or kSchedBalanced
+  int32_t part_tokens;    // fixed: tokens per partition (multiple of 16)
+  int32_t num_parts;      // fixed: partitions per sequence in the grid (>= 1)
+  int32_t nwc;            // balanced: workgroups per unit chunk
+  int32_t split;          // 1: pieces may leave triples, merged afterwards
   float qk_scale_log2;    // scale * k_scale * log2(e)
   float v_scale;          // fp8 V scale (1 otherwise)
 };

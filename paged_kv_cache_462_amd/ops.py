@@ -90,10 +90,19 @@ def decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, head
                                                   block_size, max_blocks, partition_tokens))
 
 
-def decode_plan_partition(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                          block_size: int, max_blocks: int, partition_tokens: int = 0) -> int:
-    return check(load().pa_decode_plan_partition(batch, num_q_heads, num_kv_heads, head_dim,
-                                                 block_size, max_blocks, partition_tokens))
+SCHEDULE_NAMES = {_lib.PA_SCHEDULE_SINGLE: "single", _lib.PA_SCHEDULE_PARTITIONS: "partitions",
+                  _lib.PA_SCHEDULE_BALANCED: "balanced"}
+
+
+def decode_plan(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, max_blocks: int, partition_tokens: int = 0) -> dict:
+    """pa_decode_plan: {"schedule": "single" | "partitions" | "balanced",
+    "partition_tokens": int, "workspace_bytes": int}."""
+    info = _lib.PaDecodePlan()
+    check(load().pa_decode_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks, partition_tokens, byref(info)))
+    return {"schedule": SCHEDULE_NAMES[info.schedule], "partition_tokens": info.partition_tokens,
+            "workspace_bytes": info.workspace_bytes}
 
 
 def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

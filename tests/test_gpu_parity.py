@@ -296,3 +296,73 @@ def test_full_size(name):
     ref = G.oracle_decode(wl, kc, vc, pairs)
     atol, rtol = G.tol_for(wl)
     G.assert_close(out, ref, atol, rtol, pairs=pairs, what=f"full {name}")
+
+
+# --- the balanced schedule (automatic plan) -------------------------------------
+
+def _random_lengths(B, hi, seed, zero_frac=0.1):
+    rng = np.random.default_rng(seed)
+    L = rng.integers(1, hi + 1, B)
+    L[rng.random(B) < zero_frac] = 0
+    return [int(x) for x in L]
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5"])
+def test_balanced_many_sequences(name):
+    """More sequences than workgroups, empty ones among them: every piece
+    boundary pattern of the balanced schedule, against the oracle."""
+    lens = _random_lengths(300, 200, seed=11)
+    cfg = shrink(get_config(name), batch=300, lengths=("list", lens))
+    wl = make_workload(cfg, seed=12)
+    plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                          cfg.block_size, wl.max_blocks, 0)
+    assert plan["schedule"] == "balanced"
+    G.say(f"balanced many sequences {name}")
+    kc, vc = G.oracle_caches(wl)
+    d = G.to_device(wl)
+    for path in (VALU, MFMA):
+        out = G.gpu_decode(wl, d, partition_tokens=0, path=path)
+        torch.cuda.synchronize()
+        ref = G.oracle_decode(wl, kc, vc)
+        atol, rtol = G.tol_for(wl)
+        G.assert_close(out, ref, atol, rtol, what=f"balanced {name} path={path}")
+
+
+@pytest.mark.parametrize("B,schedule", [(2048, "balanced"), (2049, "single")])
+def test_balanced_batch_limit(B, schedule):
+    """The largest batch the balanced schedule takes, and the first one past
+    it (512-token partitions instead, which for these short sequences is one
+    pass per sequence)."""
+    lens = _random_lengths(B, 40, seed=B)
+    cfg = shrink(get_config("c3"), batch=B, lengths=("list", lens))
+    wl = make_workload(cfg, seed=13)
+    plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                          cfg.block_size, wl.max_blocks, 0)
+    assert plan["schedule"] == schedule
+    G.say(f"balanced batch limit B={B}")
+    kc, vc = G.oracle_caches(wl)
+    d = G.to_device(wl)
+    out = G.gpu_decode(wl, d, partition_tokens=0)
+    torch.cuda.synchronize()
+    pairs = G.sample_pairs(wl, 64)
+    pairs += [(b, 0) for b in range(B) if lens[b] == 0][:8]
+    ref = G.oracle_decode(wl, kc, vc, pairs)
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(out, ref, atol, rtol, pairs=pairs, what=f"batch limit B={B}")
+
+
+@pytest.mark.parametrize("name", ["c2", "c4", "c5"])
+def test_balanced_matches_single(name):
+    """Balanced pieces merged = one pass over each whole sequence, within the
+    16-bit tolerance, and reruns are bit-identical."""
+    wl, kc, vc, _ = _small(name)
+    G.say(f"balanced vs single {name}")
+    d = G.to_device(wl)
+    a = G.gpu_decode(wl, d, partition_tokens=-1).double()
+    b1 = G.gpu_decode(wl, d, partition_tokens=0)
+    b2 = G.gpu_decode(wl, d, partition_tokens=0)
+    torch.cuda.synchronize()
+    assert torch.equal(b1, b2)
+    atol, rtol = G.tol_for(wl)
+    err = (b1.double() - a).abs()
+    assert bool((err <= atol + rtol * a.abs()).all())

@@ -134,15 +134,35 @@ def test_decode_rejects_mfma_for_f32():
     _expect(_call_decode(a, ln), _lib.PA_ERR_UNSUPPORTED)
 
 
+def _plan(*args):
+    info = _lib.PaDecodePlan()
+    rc = _lib.load().pa_decode_plan(*args, ctypes.byref(info))
+    return rc, info
+
+
 def test_plan():
     lib = _lib.load()
-    assert lib.pa_decode_plan_partition(32, 32, 32, 128, 16, 128, 0) == 512
-    assert lib.pa_decode_plan_partition(32, 32, 32, 128, 16, 32, 0) == 0      # 512 tokens: one partition
-    assert lib.pa_decode_plan_partition(4, 32, 8, 128, 16, 2048, -1) == 0
-    assert lib.pa_decode_plan_partition(4, 32, 8, 128, 16, 2048, 1024) == 1024
-    assert lib.pa_decode_plan_partition(4, 32, 8, 128, 16, 2048, 100) == _lib.PA_ERR_INVALID_ARG
+    B_ = _lib.PA_SCHEDULE_BALANCED
+    # automatic: balanced shares of the batch's tiles
+    rc, info = _plan(32, 32, 32, 128, 16, 128, 0)
+    assert rc == 0 and info.schedule == B_ and info.partition_tokens == 0
+    slots = 256 + 32
+    assert info.workspace_bytes == slots * 32 * 130 * 4 + 32 * 8
+    assert lib.pa_decode_workspace_bytes(32, 32, 32, 128, 16, 128, 0) == info.workspace_bytes
+    # automatic with a batch beyond the balanced limit: 512-token partitions
+    rc, info = _plan(4096, 8, 8, 128, 16, 128, 0)
+    assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_PARTITIONS and info.partition_tokens == 512
+    rc, info = _plan(4, 32, 8, 128, 16, 2048, -1)
+    assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_SINGLE and info.workspace_bytes == 0
+    rc, info = _plan(4, 32, 8, 128, 16, 2048, 1024)
+    assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_PARTITIONS and info.partition_tokens == 1024
+    rc, info = _plan(32, 32, 32, 128, 16, 32, 512)      # 512 tokens: one partition
+    assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_SINGLE
+    rc, _ = _plan(4, 32, 8, 128, 16, 2048, 100)
+    assert rc == _lib.PA_ERR_INVALID_ARG
     assert lib.pa_decode_workspace_bytes(4, 32, 8, 128, 16, 2048, 512) == 4 * 32 * 64 * 130 * 4
     assert lib.pa_decode_workspace_bytes(4, 32, 8, 128, 16, 2048, -1) == 0
+    assert lib.pa_decode_plan(4, 32, 8, 128, 16, 2048, 0, None) == _lib.PA_ERR_INVALID_ARG
 
 
 def _cw_args(T=4, Hkv=2, D=128, N=10, bs=16, sdt=_lib.PA_BF16, cdt=_lib.PA_BF16, scale=1.0):
