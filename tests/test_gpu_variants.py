@@ -1,0 +1,73 @@
+"""Every decode variant the library builds, against the CPU oracle (GPU).
+
+The five workloads reach only some of the kernel variants (query / KV dtype
+pairs, head_dim, query heads per kv head, block size, VALU or MFMA inner
+loop).  This matrix reaches the rest, each on a small batch with ragged
+lengths (an empty sequence, a partly filled last block, sequences longer
+than a 512-token partition) and each under the three schedules: balanced
+(automatic), fixed 48-token partitions, and one pass per sequence."""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_462_amd as pa
+from synth.configs import WorkloadConfig
+from synth.generate import make_workload
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+LENS = [0, 1, 37, 300, 700, 1500]
+
+# (query dtype, kv dtype): every pair the library accepts
+PAIRS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("f16", "fp8"), ("bf16", "fp8")]
+
+
+def _variants():
+    out = []
+    for (qd, kd), D, group, bs in itertools.product(PAIRS, (64, 128), (1, 2, 4, 8), (16, 32)):
+        paths = [pa.PATH_VALU] if qd == "f32" else [pa.PATH_VALU, pa.PATH_MFMA]
+        for path in paths:
+            out.append((qd, kd, D, group, bs, path))
+    return out
+
+
+def _case(qd, kd, D, group, bs):
+    hkv = 2
+    cfg = WorkloadConfig(
+        name=f"variant_{qd}_{kd}_d{D}_g{group}_bs{bs}", description="variant matrix case",
+        batch=len(LENS), num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=D, block_size=bs,
+        q_dtype=qd, kv_dtype=kd, lengths=("list", LENS), seed=500 + D + group + bs)
+    wl = make_workload(cfg)
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_decode(wl, kc, vc)
+    return wl, kc, vc, ref
+
+
+_cache = {}
+
+
+@pytest.mark.parametrize("qd,kd,D,group,bs,path", _variants())
+def test_variant_matches_oracle(qd, kd, D, group, bs, path):
+    key = (qd, kd, D, group, bs)
+    if key not in _cache:
+        _cache.clear()
+        _cache[key] = _case(*key)
+    wl, kc, vc, ref = _cache[key]
+    G.say(f"variant q={qd} kv={kd} D={D} group={group} bs={bs} path={path}")
+    d = G.to_device(wl)
+    torch.cuda.synchronize()
+    assert G.caches_equal(d.kc, kc) and G.caches_equal(d.vc, vc)
+    atol, rtol = G.tol_for(wl)
+    outs = []
+    for pt in (0, 48, -1):
+        out = G.gpu_decode(wl, d, partition_tokens=pt, path=path)
+        torch.cuda.synchronize()
+        G.assert_close(out, ref, atol, rtol, what=f"{key} path={path} partition={pt}")
+        outs.append(out)
+    # the empty sequence gives a zero row under every schedule
+    for out in outs:
+        assert torch.equal(out[0].float(), torch.zeros_like(out[0].float()))
