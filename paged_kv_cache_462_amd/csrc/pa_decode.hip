@@ -181,6 +181,20 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
     // sequence is processed by workgroup first + k)
     const int NW = min(p.nwc, T);
     const int wi = blockIdx.y;
+    if (blockIdx.x == 0 && wi == 0) {
+      // the merge kernel's plan: (first slot, pieces) of every sequence,
+      // 0 pieces for an empty one
+      for (int b = threadIdx.x; b < p.B; b += blockDim.x) {
+        const int sb = s_pref[b], se = s_pref[b + 1];
+        int first = 0, pieces = 0;
+        if (se > sb) {
+          first = tile_owner(sb, T, NW);
+          pieces = tile_owner(se - 1, T, NW) - first + 1;
+        }
+        p.ws_meta[2 * b] = first + b;
+        p.ws_meta[2 * b + 1] = pieces;
+      }
+    }
     if (!has_unit || wi >= NW) return;
     const int tb = (int)((int64_t)wi * T / NW);
     const int te = (int)((int64_t)(wi + 1) * T / NW);
@@ -199,10 +213,6 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
       const int pieces = tile_owner(se - 1, T, NW) - first + 1;
       const int a = max(tb, sb) - sb;
       const int e = min(te, se) - sb;
-      if (a == 0 && blockIdx.x == 0 && threadIdx.x == 0) {
-        p.ws_meta[2 * b] = first + b;
-        p.ws_meta[2 * b + 1] = pieces;
-      }
       Work wk;
       wk.b = b;
       wk.L = clamp_len(p, b);
@@ -848,38 +858,43 @@ __global__ __launch_bounds__(kMaxThreads) void decode_valu_kernel(const DecodePa
 
 // ============================================================================
 // Piece merge: out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) with
-// M = max_p m_p.  One 256-thread workgroup per (query head, sequence): a
-// workgroup-wide max over the pieces, then GROUPS groups of D/4 threads
-// (4 dims each, 16-byte loads) take every GROUPS-th piece, and the group
-// partial sums are added in group order (a fixed order: the result does not
-// depend on timing).  Under the balanced schedule it also writes the zero
-// rows of empty sequences (no piece exists for them).
+// M = max_p m_p.  One 256-thread workgroup per (query head, sequence):
+// GROUPS groups of D/4 threads (4 dims each, 16-byte loads) each fold every
+// GROUPS-th piece into a running (max, sum, output), loads of up to four
+// pieces in flight at once; then the group states are combined in group
+// order (a fixed order: the result does not depend on timing).  The piece
+// plan comes from the decode kernel (balanced schedule: per-sequence first
+// slot and piece count, 0 pieces for an empty sequence, whose zero row is
+// written here) or from the partition size (fixed schedule).
 // ============================================================================
 constexpr int kMergeThreads = 256;
 
 template <int QK, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams p) {
   constexpr int TPR = D / 4;                   // threads per piece row
-  constexpr int GROUPS = kMergeThreads / TPR;  // pieces summed side by side
-  __shared__ float s_red[kMergeThreads / 64];
+  constexpr int GROUPS = kMergeThreads / TPR;  // pieces folded side by side
+  constexpr int U = 4;                         // pieces in flight per group
   __shared__ f32x4 s_num[GROUPS][TPR];
-  __shared__ float s_den[GROUPS];
+  __shared__ float s_m[GROUPS], s_den[GROUPS];
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int L = clamp_len(p, b);
   const int64_t ob = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
   int slot0, P;
   if (p.sched == kSchedBalanced) {
-    if (L == 0) {
-      if (tid < D) store_out<QK>(p.out, ob + tid, 0.f);
-      return;
-    }
     slot0 = p.ws_meta[2 * b];
     P = p.ws_meta[2 * b + 1];
-    if (P <= 1) return;  // single piece: written directly
+    if (P == 0) {
+      if (tid < TPR) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        store_out_vec<QK, 4>(p.out, ob + 4 * tid, z);
+      }
+      return;
+    }
+    if (P == 1) return;  // single piece: written directly
   } else {
+    const int L = clamp_len(p, b);
     if (L <= p.part_tokens) return;  // single partition: written directly
     slot0 = b * p.num_parts;
     P = (L + p.part_tokens - 1) / p.part_tokens;
@@ -888,41 +903,60 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams
   const int64_t base = triple_index(p, slot0, h);
   const int64_t step = p.Hq;
 
-  float M = kMaxFloor;
-  for (int q = tid; q < P; q += kMergeThreads) M = fmaxf(M, p.ws_ml[2 * (base + q * step)]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((tid & 63) == 0) s_red[tid >> 6] = M;
-  __syncthreads();
-  M = s_red[0];
-#pragma unroll
-  for (int k = 1; k < kMergeThreads / 64; ++k) M = fmaxf(M, s_red[k]);
-
   const int grp = tid / TPR;
   const int c = tid - grp * TPR;
+  float M = kMaxFloor, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-#pragma unroll 4
-  for (int q = grp; q < P; q += GROUPS) {
-    const int64_t ti = base + q * step;
-    const float sc = fast_exp2(p.ws_ml[2 * ti] - M);
-    den += p.ws_ml[2 * ti + 1] * sc;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p.ws_acc + ti * D + 4 * c);
-    num += a * sc;
+  for (int q0 = grp; q0 < P; q0 += U * GROUPS) {
+    float mq[U], lq[U];
+    f32x4 aq[U];
+    // unconditional loads (a piece past the end reloads the last one and is
+    // masked afterwards), so all of them are in flight together
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = min(q0 + u * GROUPS, P - 1);
+      const int64_t ti = base + q * step;
+      mq[u] = p.ws_ml[2 * ti];
+      lq[u] = p.ws_ml[2 * ti + 1];
+      aq[u] = *reinterpret_cast<const f32x4*>(p.ws_acc + ti * D + 4 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (q0 + u * GROUPS >= P) {
+        mq[u] = kMaxFloor;
+        lq[u] = 0.f;
+        aq[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float mn = fmaxf(M, mq[u]);
+      const float s_old = fast_exp2(M - mn), s_new = fast_exp2(mq[u] - mn);
+      den = den * s_old + lq[u] * s_new;
+      num = num * s_old + aq[u] * s_new;
+      M = mn;
+    }
   }
   s_num[grp][c] = num;
-  if (c == 0) s_den[grp] = den;
+  if (c == 0) {
+    s_m[grp] = M;
+    s_den[grp] = den;
+  }
   __syncthreads();
   if (tid >= TPR) return;
-  f32x4 tot = s_num[0][tid];
-  float dtot = s_den[0];
+  float Mt = s_m[0];
 #pragma unroll
-  for (int k = 1; k < GROUPS; ++k) {
-    tot += s_num[k][tid];
-    dtot += s_den[k];
+  for (int k = 1; k < GROUPS; ++k) Mt = fmaxf(Mt, s_m[k]);
+  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+  float dtot = 0.f;
+#pragma unroll
+  for (int k = 0; k < GROUPS; ++k) {
+    const float sc = fast_exp2(s_m[k] - Mt);
+    tot += s_num[k][tid] * sc;
+    dtot += s_den[k] * sc;
   }
   const float sc = dtot > 0.f ? p.v_scale / dtot : 0.f;
-  float x[4] = {tot[0] * sc, tot[1] * sc, tot[2] * sc, tot[3] * sc};
+  const float x[4] = {tot[0] * sc, tot[1] * sc, tot[2] * sc, tot[3] * sc};
   store_out_vec<QK, 4>(p.out, ob + 4 * tid, x);
 }
 

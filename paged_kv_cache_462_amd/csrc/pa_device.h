@@ -175,54 +175,4 @@ __device__ __forceinline__ void load_lds16(const void* src, void* lds_base) {
                                    kNonTemporalAux);
 }
 
-// s_waitcnt immediate that waits until at most N vector memory operations
-// of this wave are outstanding and leaves the other counters alone
-// (vmcnt in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
-template <int N>
-struct VmcntImm {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  static constexpr int v = (N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14);
-};
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(VmcntImm<N>::v);
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// LDS byte offset of a pointer into __shared__ memory.
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// R 16-byte LDS reads (ds_read_b128) and the wait for their data, as one
-// unit the compiler does not look into: it therefore adds no wait of its
-// own for earlier load-to-LDS operations (the caller orders those with
-// wait_vmcnt), and no instruction that uses the results can be placed
-// before the data has arrived.
-template <int R>
-__device__ __forceinline__ void lds_read16x(i32x4 (&out)[R], const uint32_t (&addr)[R]);
-
-template <>
-__device__ __forceinline__ void lds_read16x<1>(i32x4 (&out)[1], const uint32_t (&a)[1]) {
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(out[0]) : "v"(a[0]) : "memory");
-}
-template <>
-__device__ __forceinline__ void lds_read16x<2>(i32x4 (&out)[2], const uint32_t (&a)[2]) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(out[0]), "=&v"(out[1])
-               : "v"(a[0]), "v"(a[1])
-               : "memory");
-}
-template <>
-__device__ __forceinline__ void lds_read16x<4>(i32x4 (&out)[4], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
-      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-      : "memory");
-}
-
 }  // namespace pa
