@@ -252,6 +252,45 @@ int32_t pa_bm_num_blocks_of(const pa_block_manager* m, int64_t seq_id);
 int pa_bm_export(const pa_block_manager* m, const int64_t* seq_ids, int32_t n,
                  int32_t max_blocks, int32_t* block_tables, int32_t* seq_lens);
 
+/* ------------------------------------------------------------------------ *
+ * Prefix cache ("KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践",
+ * `HashBasedCaching`: block hashing and the prefix lookup walk-through, where
+ * tokens [A,B,C,D,E,F] in 2-token blocks find blocks 7 and 3 for [A,B] and
+ * [C,D] and need a new block for [E,F]; "5.KV Cache 管理 & PagedAttention",
+ * question 20).  Maps the leading full blocks of token sequences to the
+ * physical blocks that hold their K/V.  Block i's key is the whole token
+ * prefix up to the end of block i (equal block contents after different
+ * histories do not match); hits are verified token by token, so a hash
+ * collision never yields a wrong block.  The cache holds one allocator
+ * reference on every cached block.  Plain CPU code, thread-safe.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_prefix_cache pa_prefix_cache;
+
+/* NULL on invalid arguments.  The allocator must outlive the cache. */
+pa_prefix_cache* pa_pc_create(pa_allocator* a, int32_t block_size);
+/* Releases the cache's references. */
+void pa_pc_destroy(pa_prefix_cache* c);
+/* Longest cached run of leading full blocks of tokens[0..n_tokens):
+ * writes their physical ids to blocks_out[0..k) (k <= max_blocks), takes
+ * one reference on each for the caller (release with pa_alloc_decref, e.g.
+ * after pa_bm_add_sequence has taken its own), and returns k, or a
+ * negative status. */
+int32_t pa_pc_match(pa_prefix_cache* c, const int32_t* tokens, int64_t n_tokens,
+                    int32_t* blocks_out, int32_t max_blocks);
+/* Caches the leading full blocks of a sequence: block i (i < n_blocks and
+ * (i + 1) * block_size <= n_tokens) holds the K/V of tokens up to the end of
+ * block i.  Prefixes already cached keep their block; every newly cached
+ * block gets one cache reference.  Returns the number newly cached, or a
+ * negative status (PA_ERR_BAD_BLOCK for a block that is not allocated). */
+int32_t pa_pc_insert(pa_prefix_cache* c, const int32_t* tokens, int64_t n_tokens,
+                     const int32_t* blocks, int32_t n_blocks);
+/* Releases up to max_blocks cached blocks that nobody else references,
+ * least recently matched or inserted first, leaves of the prefix tree
+ * only.  Returns the number released. */
+int32_t pa_pc_evict(pa_prefix_cache* c, int32_t max_blocks);
+/* Number of cached blocks. */
+int32_t pa_pc_size(const pa_prefix_cache* c);
+
 #ifdef __cplusplus
 }
 #endif

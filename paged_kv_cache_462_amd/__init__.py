@@ -13,6 +13,7 @@ from .ops import (  # noqa: F401
     PATH_VALU,
     BlockAllocator,
     BlockManager,
+    PrefixCache,
     build_info,
     copy_blocks,
     decode,

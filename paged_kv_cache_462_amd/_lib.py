@@ -53,6 +53,7 @@ _T = POINTER(PaTensor)
 _L = POINTER(PaLaunch)
 _A = c_void_p  # pa_allocator*
 _M = c_void_p  # pa_block_manager*
+_P = c_void_p  # pa_prefix_cache*
 
 SIGNATURES = {
     "pa_reshape_and_cache": (c_int32, [_T, _T, _T, _T, _T, _L]),
@@ -79,6 +80,12 @@ SIGNATURES = {
     "pa_bm_seq_len": (c_int64, [_M, c_int64]),
     "pa_bm_num_blocks_of": (c_int32, [_M, c_int64]),
     "pa_bm_export": (c_int32, [_M, POINTER(c_int64), c_int32, c_int32, POINTER(c_int32), POINTER(c_int32)]),
+    "pa_pc_create": (_P, [_A, c_int32]),
+    "pa_pc_destroy": (None, [_P]),
+    "pa_pc_match": (c_int32, [_P, POINTER(c_int32), c_int64, POINTER(c_int32), c_int32]),
+    "pa_pc_insert": (c_int32, [_P, POINTER(c_int32), c_int64, POINTER(c_int32), c_int32]),
+    "pa_pc_evict": (c_int32, [_P, c_int32]),
+    "pa_pc_size": (c_int32, [_P]),
 }
 
 _LIB = None

@@ -236,3 +236,49 @@ class BlockManager:
                                      tables.ctypes.data_as(ctypes.POINTER(c_int32)),
                                      lens.ctypes.data_as(ctypes.POINTER(c_int32))))
         return tables, lens
+
+
+class PrefixCache:
+    """pa_pc_*: prefix cache mapping leading full blocks of token sequences
+    to the physical blocks that hold their K/V (host)."""
+
+    def __init__(self, allocator: BlockAllocator, block_size: int):
+        self._lib = load()
+        self._alloc = allocator  # keep alive: the cache releases through it
+        h = self._lib.pa_pc_create(allocator.handle, int(block_size))
+        if not h:
+            raise _lib.PaError(_lib.PA_ERR_INVALID_ARG, _lib.last_error())
+        self._h = h
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pa_pc_destroy(h)
+            self._h = None
+
+    @staticmethod
+    def _ints(xs, dtype=np.int32):
+        arr = np.ascontiguousarray(np.asarray(list(xs), dtype=dtype))
+        return arr, (arr.ctypes.data_as(ctypes.POINTER(c_int32)) if len(arr) else None)
+
+    def match(self, tokens: Sequence[int], max_blocks: Optional[int] = None):
+        """Physical ids of the longest cached run of leading full blocks; the
+        caller receives one reference on each."""
+        tok, tp = self._ints(tokens)
+        n = len(tok) // self.block_size if max_blocks is None else int(max_blocks)
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        k = check(self._lib.pa_pc_match(self._h, tp, len(tok),
+                                        out.ctypes.data_as(ctypes.POINTER(c_int32)), n))
+        return out[:k].tolist()
+
+    def insert(self, tokens: Sequence[int], blocks: Sequence[int]) -> int:
+        tok, tp = self._ints(tokens)
+        blk, bp = self._ints(blocks)
+        return check(self._lib.pa_pc_insert(self._h, tp, len(tok), bp, len(blk)))
+
+    def evict(self, max_blocks: int) -> int:
+        return check(self._lib.pa_pc_evict(self._h, int(max_blocks)))
+
+    def size(self) -> int:
+        return check(self._lib.pa_pc_size(self._h))

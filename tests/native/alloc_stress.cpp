@@ -103,6 +103,47 @@ int main(int argc, char** argv) {
   for (int t = 0; t < kThreads; ++t) th.emplace_back(work, t);
   for (auto& x : th) x.join();
 
+  // prefix cache shared by all threads: prompts built from a few common
+  // stems; match, allocate the rest, cache, release, evict
+  pa_prefix_cache* pc = pa_pc_create(a, bs);
+  CHECK(pc != nullptr);
+  auto prefix_work = [&](int t) {
+    std::mt19937 rng(777 + t);
+    std::vector<std::vector<int32_t>> held;
+    for (int op = 0; op < kOps / 4; ++op) {
+      std::vector<int32_t> toks(bs * (1 + rng() % 6));
+      const int stem = rng() % 3;
+      for (size_t i = 0; i < toks.size(); ++i)
+        toks[i] = i < (size_t)bs * 2 ? stem * 100 + (int)i : (int)(rng() % 4);
+      const int32_t nb = (int32_t)(toks.size() / bs);
+      std::vector<int32_t> table(nb);
+      const int32_t k = pa_pc_match(pc, toks.data(), (int64_t)toks.size(), table.data(), nb);
+      CHECK(k >= 0 && k <= nb);
+      bool ok = k >= 0;
+      int32_t got = k < 0 ? 0 : k;
+      while (ok && got < nb) {
+        if (pa_alloc_allocate(a, &table[got]) == PA_OK) ++got;
+        else ok = false;
+      }
+      if (ok) CHECK(pa_pc_insert(pc, toks.data(), (int64_t)toks.size(), table.data(), nb) >= 0);
+      table.resize(got);
+      held.push_back(table);
+      if (rng() % 2 && !held.empty()) {
+        for (int32_t b : held.front()) CHECK(pa_alloc_decref(a, b) == PA_OK);
+        held.erase(held.begin());
+      }
+      if (rng() % 8 == 0) CHECK(pa_pc_evict(pc, 4) >= 0);
+    }
+    for (auto& tb : held)
+      for (int32_t b : tb) CHECK(pa_alloc_decref(a, b) == PA_OK);
+  };
+  th.clear();
+  for (int t = 0; t < kThreads; ++t) th.emplace_back(prefix_work, t);
+  for (auto& x : th) x.join();
+  CHECK(pa_pc_evict(pc, N) == pa_pc_size(pc) || pa_pc_size(pc) == 0);
+  CHECK(pa_pc_size(pc) == 0);
+  pa_pc_destroy(pc);
+
   // only the shared prefix is still held, once each
   CHECK(pa_alloc_num_free(a) == N - n_shared);
   for (int32_t b : shared) CHECK(pa_alloc_refcount(a, b) == 1);

@@ -1,10 +1,11 @@
 """The host block allocator and block manager under ThreadSanitizer and
 AddressSanitizer + UndefinedBehaviorSanitizer (CPU).
 
-tests/native/alloc_stress.cpp drives one allocator and one manager from
-several threads (sequences with shared prefix blocks, appends with
-copy-on-write, forks, frees, direct allocate / incref / decref, exports)
-and checks the pool is whole at the end.  It is built here with g++ from
+tests/native/alloc_stress.cpp drives one allocator, one block manager and
+one prefix cache from several threads (sequences with shared prefix
+blocks, appends with copy-on-write, forks, frees, direct allocate / incref /
+decref, exports; prefix matches, inserts, releases and evictions) and
+checks the pool is whole at the end.  It is built here with g++ from
 the allocator's source alone (host code, no device code involved)."""
 
 import os
@@ -15,6 +16,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = [os.path.join(ROOT, "paged_kv_cache_462_amd", "csrc", "pa_alloc.cpp"),
+       os.path.join(ROOT, "paged_kv_cache_462_amd", "csrc", "pa_prefix.cpp"),
        os.path.join(ROOT, "tests", "native", "alloc_stress.cpp")]
 
 pytestmark = pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")

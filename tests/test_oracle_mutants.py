@@ -120,3 +120,35 @@ def test_fp8_table_mutant_is_caught(monkeypatch):
     monkeypatch.setattr(fp8, "decode_table", _bias8_table)
     with pytest.raises(AssertionError):
         TF.test_decode_table_matches_torch()
+
+
+def test_prefix_cache_mutants_are_caught(monkeypatch):
+    """Keying a block by its own tokens only (content hash, no history), or
+    matching without taking references, fails the prefix-cache pins."""
+    from oracle import prefix_cache as PC
+    from tests import test_prefix_cache as TP
+
+    TP.test_same_block_after_other_history_does_not_match()
+    TP.test_page_example_block_table()
+
+    def own_tokens(self, tokens, count):
+        t = tuple(int(x) for x in tokens)
+        return [t[i * self.bs:(i + 1) * self.bs] for i in range(count)]
+
+    with monkeypatch.context() as mp:
+        mp.setattr(PC.PrefixCacheModel, "_prefixes", own_tokens)
+        with pytest.raises(AssertionError):
+            TP.test_same_block_after_other_history_does_not_match()
+
+    real_match = PC.PrefixCacheModel.match
+
+    def match_without_refs(self, tokens, max_blocks=None):
+        out = real_match(self, tokens, max_blocks)
+        for b in out:
+            self.alloc.decref(b)
+        return out
+
+    with monkeypatch.context() as mp:
+        mp.setattr(PC.PrefixCacheModel, "match", match_without_refs)
+        with pytest.raises(AssertionError):
+            TP.test_page_example_block_table()
