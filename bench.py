@@ -115,6 +115,86 @@ def cpu_baseline(wl, seconds: float):
     }
 
 
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def bench_swap(args) -> int:
+    """Every KV block of the workload's batch swapped out to a pinned host
+    pool and back in, each direction timed with HIP events on the launch
+    stream; bytes = K and V of the blocks moved, against the host link."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_462_amd as pa
+    from synth import get_config, make_workload
+
+    cfg = get_config(args.config)
+    wl = make_workload(cfg)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    fp8 = c.kv_dtype == "fp8"
+    st = torch.uint8 if fp8 else wl.tok_key.dtype
+    shape = (wl.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    kc = torch.zeros(shape, dtype=st, device=dev)
+    vc = torch.zeros(shape, dtype=st, device=dev)
+    pa.reshape_and_cache(wl.tok_key.to(dev), wl.tok_value.to(dev),
+                         torch.from_numpy(wl.slot_mapping).to(dev), kc, vc,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype="fp8" if fp8 else None)
+    used = np.unique(wl.block_tables[wl.block_tables >= 0])
+    n = len(used)
+    hk = torch.empty((n,) + shape[1:], dtype=st).pin_memory()
+    hv = torch.empty((n,) + shape[1:], dtype=st).pin_memory()
+    out_pairs = torch.from_numpy(np.stack([used, np.arange(n)], 1).astype(np.int32)).to(dev)
+    in_pairs = torch.from_numpy(np.stack([np.arange(n), used], 1).astype(np.int32)).to(dev)
+    kind = "fp8" if fp8 else None
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pa.swap_blocks(hk, hv, kc, vc, out_pairs, kv_dtype=kind)
+        pa.swap_blocks(kc, vc, hk, hv, in_pairs, kv_dtype=kind)
+    torch.cuda.synchronize()
+    t_out, t_in = [], []
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        pa.swap_blocks(hk, hv, kc, vc, out_pairs, kv_dtype=kind)
+        e[1].record(stream)
+        pa.swap_blocks(kc, vc, hk, hv, in_pairs, kv_dtype=kind)
+        e[2].record(stream)
+        e[2].synchronize()
+        t_out.append(e[0].elapsed_time(e[1]))
+        t_in.append(e[1].elapsed_time(e[2]))
+    t1 = time.perf_counter()
+    nbytes = 2 * n * int(np.prod(shape[1:])) * kc.element_size()
+    out_gbps = nbytes / (float(np.mean(t_out)) * 1e-3) / 1e9
+    in_gbps = nbytes / (float(np.mean(t_in)) * 1e-3) / 1e9
+    ms_step = (t1 - t0) * 1e3 / K
+    res = {
+        "metric": "KV block swap: device -> pinned host and back (GB/s per direction)",
+        "value": round(2 * nbytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.kv_dtype,
+        "data": "synthetic",
+        "config": {"workload": c.name, "blocks": int(n), "bytes_per_direction": int(nbytes)},
+        "swap_out_GBps": round(out_gbps, 2),
+        "swap_in_GBps": round(in_gbps, 2),
+        "roofline": {"bound": "host-link", "achieved": round(min(out_gbps, in_gbps), 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(out_gbps, in_gbps) / HOST_LINK_PEAK_GBPS, 4), "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +208,9 @@ def main() -> int:
     ap.add_argument("--hot-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", default="decode", choices=["decode", "swap"],
+                    help="decode: the decode hot path (default); swap: the batch's KV blocks "
+                         "swapped out to pinned host memory and back in (pa_swap_blocks)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -147,6 +230,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     pa.load()
+    if args.op == "swap":
+        return bench_swap(args)
     cfg = get_config(args.config)
     log(f"[bench] generating {cfg.name}")
     wl = make_workload(cfg)

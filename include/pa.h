@@ -156,6 +156,26 @@ int pa_copy_blocks(pa_tensor* key_cache, pa_tensor* value_cache,
                    const pa_tensor* block_pairs, const pa_launch* launch);
 
 /*
+ * pa_swap_blocks -- copy whole blocks from one pair of pools to another,
+ * for swapping blocks out to host memory and back in
+ * ("KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践", `CPUSwap`):
+ * for each row (src, dst) of block_pairs,
+ * dst_key_cache[dst] = src_key_cache[src], and the same for V.
+ *   dst_key_cache, dst_value_cache  [N_dst, bs, Hkv, D] contiguous
+ *   src_key_cache, src_value_cache  [N_src, bs, Hkv, D] contiguous, same
+ *                           dtype and block shape as the destination
+ *   block_pairs             [n, 2] i32, rows independent, no destination
+ *                           block twice
+ * Either pair of pools may live in pinned host memory (allocated with
+ * hipHostMalloc, e.g. torch's pin_memory), which the kernel reads or writes
+ * over the host link; block_pairs must be device-accessible.  Pairs with an
+ * id outside its pool are skipped.  Asynchronous on launch->stream.
+ */
+int pa_swap_blocks(pa_tensor* dst_key_cache, pa_tensor* dst_value_cache,
+                   const pa_tensor* src_key_cache, const pa_tensor* src_value_cache,
+                   const pa_tensor* block_pairs, const pa_launch* launch);
+
+/*
  * Workspace bytes pa_decode needs for these sizes and this partition request
  * (the same plan pa_decode makes; 0 when it does not split).  max_blocks is
  * the block-table width.  Returns a negative status on invalid sizes.

@@ -20,4 +20,5 @@ from .ops import (  # noqa: F401
     decode_plan,
     decode_workspace_bytes,
     reshape_and_cache,
+    swap_blocks,
 )

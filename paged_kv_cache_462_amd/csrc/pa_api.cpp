@@ -352,28 +352,67 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value, const pa_
   return PA_OK;
 }
 
-int pa_copy_blocks(pa_tensor* key_cache, pa_tensor* value_cache, const pa_tensor* block_pairs,
-                   const pa_launch* launch) {
+namespace {
+
+// shared checks of pa_copy_blocks / pa_swap_blocks; fills the byte size
+int check_block_copy(const pa_tensor* dk, const pa_tensor* dv, const pa_tensor* sk,
+                     const pa_tensor* sv, const pa_tensor* pairs, int64_t* block_bytes) {
   int rc;
-  if ((rc = check_cache_pair(key_cache, value_cache)) || (rc = check_tensor(block_pairs, "block_pairs", 2)))
+  if ((rc = check_cache_pair(dk, dv)) || (rc = check_cache_pair(sk, sv)) ||
+      (rc = check_tensor(pairs, "block_pairs", 2)))
     return rc;
-  if (block_pairs->dtype != PA_I32 || block_pairs->shape[1] != 2 || !contiguous(block_pairs))
+  if (sk->dtype != dk->dtype) return fail(PA_ERR_INVALID_ARG, "source and destination pools differ in dtype");
+  for (int i = 1; i < 4; ++i)
+    if (sk->shape[i] != dk->shape[i])
+      return fail(PA_ERR_INVALID_ARG, "source and destination blocks differ in shape");
+  if (pairs->dtype != PA_I32 || pairs->shape[1] != 2 || !contiguous(pairs))
     return fail(PA_ERR_INVALID_ARG, "block_pairs must be contiguous int32 [n, 2]");
-  const int64_t bytes = key_cache->shape[1] * key_cache->shape[2] * key_cache->shape[3] *
-                        elem_size(key_cache->dtype);
+  const int64_t bytes = dk->shape[1] * dk->shape[2] * dk->shape[3] * elem_size(dk->dtype);
   if (bytes % 16) return fail(PA_ERR_UNSUPPORTED, "block bytes must be a multiple of 16");
+  *block_bytes = bytes;
+  return PA_OK;
+}
+
+int launch_block_copy(const pa_tensor* dk, const pa_tensor* dv, const pa_tensor* sk,
+                      const pa_tensor* sv, const pa_tensor* pairs, int64_t bytes,
+                      const pa_launch* launch, const char* what) {
   pa::CopyBlocksParams p;
-  p.kc = key_cache->data;
-  p.vc = value_cache->data;
-  p.pairs = static_cast<const int32_t*>(block_pairs->data);
-  p.n = block_pairs->shape[0];
+  p.src_k = sk->data;
+  p.src_v = sv->data;
+  p.dst_k = dk->data;
+  p.dst_v = dv->data;
+  p.pairs = static_cast<const int32_t*>(pairs->data);
+  p.n = pairs->shape[0];
   p.block_bytes = bytes;
-  p.num_blocks = key_cache->shape[0];
+  p.src_blocks = sk->shape[0];
+  p.dst_blocks = dk->shape[0];
   if (p.n == 0) return PA_OK;
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_copy_blocks(p, stream);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "block copy launch failed: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // namespace
+
+int pa_copy_blocks(pa_tensor* key_cache, pa_tensor* value_cache, const pa_tensor* block_pairs,
+                   const pa_launch* launch) {
+  int64_t bytes;
+  int rc = check_block_copy(key_cache, value_cache, key_cache, value_cache, block_pairs, &bytes);
+  if (rc) return rc;
+  return launch_block_copy(key_cache, value_cache, key_cache, value_cache, block_pairs, bytes, launch,
+                           "block copy");
+}
+
+int pa_swap_blocks(pa_tensor* dst_key_cache, pa_tensor* dst_value_cache,
+                   const pa_tensor* src_key_cache, const pa_tensor* src_value_cache,
+                   const pa_tensor* block_pairs, const pa_launch* launch) {
+  int64_t bytes;
+  int rc = check_block_copy(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache,
+                            block_pairs, &bytes);
+  if (rc) return rc;
+  return launch_block_copy(dst_key_cache, dst_value_cache, src_key_cache, src_value_cache,
+                           block_pairs, bytes, launch, "block swap");
 }
 
 }  // extern "C"

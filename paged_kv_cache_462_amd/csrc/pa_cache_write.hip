@@ -8,7 +8,11 @@
 // quantisation) of 16-byte chunks; each thread owns 8 elements.
 //
 // Block copy: the device half of copy-on-write (same page, question 18,
-// copy_block), whole blocks with 16-byte loads and stores.
+// copy_block), and block swap between a device pool and a pool in pinned
+// host memory ("KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践",
+// `CPUSwap`): whole blocks with 16-byte loads and stores, thousands in
+// flight, so a swap runs at the host link's rate without a copy call per
+// block.
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -112,13 +116,13 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const CopyBlocksP
   const int64_t c = i - pair * chunks;
   const int64_t src = p.pairs[2 * pair];
   const int64_t dst = p.pairs[2 * pair + 1];
-  if (src < 0 || dst < 0 || src >= p.num_blocks || dst >= p.num_blocks) return;
+  if (src < 0 || dst < 0 || src >= p.src_blocks || dst >= p.dst_blocks) return;
   const int64_t so = src * p.block_bytes + c * 16;
   const int64_t d_o = dst * p.block_bytes + c * 16;
-  const i32x4 k = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.kc) + so);
-  const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.vc) + so);
-  *reinterpret_cast<i32x4*>(static_cast<char*>(p.kc) + d_o) = k;
-  *reinterpret_cast<i32x4*>(static_cast<char*>(p.vc) + d_o) = v;
+  const i32x4 k = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.src_k) + so);
+  const i32x4 v = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.src_v) + so);
+  *reinterpret_cast<i32x4*>(static_cast<char*>(p.dst_k) + d_o) = k;
+  *reinterpret_cast<i32x4*>(static_cast<char*>(p.dst_v) + d_o) = v;
 }
 
 }  // namespace

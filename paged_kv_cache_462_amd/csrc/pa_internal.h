@@ -79,13 +79,18 @@ struct CacheWriteParams {
 hipError_t launch_cache_write(const CacheWriteParams& p, int src_kind,
                               int cache_kind, hipStream_t stream);
 
+// Whole-block copies from one pair of pools to another (the same pools for
+// copy-on-write; a device pool and a pool in pinned host memory for swap).
 struct CopyBlocksParams {
-  void* kc;
-  void* vc;
-  const int32_t* pairs;   // [n, 2]
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int32_t* pairs;   // [n, 2] (source block, destination block)
   int64_t n;
   int64_t block_bytes;    // bytes of one physical block (bs * Hkv * D * esize)
-  int64_t num_blocks;
+  int64_t src_blocks;     // pool sizes; pairs outside them are skipped
+  int64_t dst_blocks;
 };
 
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);

@@ -136,6 +136,20 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs:
     check(load().pa_copy_blocks(*(byref(a) for a in args), byref(ln)))
 
 
+def swap_blocks(dst_key_cache: torch.Tensor, dst_value_cache: torch.Tensor,
+                src_key_cache: torch.Tensor, src_value_cache: torch.Tensor,
+                block_pairs: torch.Tensor, kv_dtype: Optional[str] = None,
+                stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_swap_blocks: dst_*[dst] = src_*[src] per (src, dst) pair; either
+    pair of pools may be pinned host memory."""
+    fp8 = _is_fp8(dst_key_cache, kv_dtype)
+    args = (_desc(dst_key_cache, fp8, 1.0), _desc(dst_value_cache, fp8, 1.0),
+            _desc(src_key_cache, fp8, 1.0), _desc(src_value_cache, fp8, 1.0), _desc(block_pairs))
+    dev = dst_key_cache if dst_key_cache.is_cuda else src_key_cache
+    ln = _launch(dev, stream=stream)
+    check(load().pa_swap_blocks(*(byref(a) for a in args), byref(ln)))
+
+
 def build_info() -> str:
     return load().pa_build_info().decode()
 

@@ -366,3 +366,36 @@ def test_balanced_matches_single(name):
     atol, rtol = G.tol_for(wl)
     err = (b1.double() - a).abs()
     assert bool((err <= atol + rtol * a.abs()).all())
+
+
+def test_swap_out_and_in_bit_exact():
+    """Blocks swapped out to a pinned host pool and back in are the same
+    bytes; blocks not named in the pairs stay untouched."""
+    G.say("swap out / in")
+    rng = np.random.default_rng(6)
+    shape = (40, 16, 4, 128)
+    kc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    hk = torch.full((24,) + shape[1:], float("nan"), dtype=torch.bfloat16).pin_memory()
+    hv = torch.full((24,) + shape[1:], float("nan"), dtype=torch.bfloat16).pin_memory()
+    src = rng.choice(40, 12, replace=False)
+    dst = rng.choice(24, 12, replace=False)
+    out_pairs = torch.from_numpy(np.stack([src, dst], 1).astype(np.int32)).cuda()
+    pa.swap_blocks(hk, hv, kc, vc, out_pairs)
+    torch.cuda.synchronize()
+    k0, v0 = kc.cpu(), vc.cpu()
+    idx_s, idx_d = torch.from_numpy(src), torch.from_numpy(dst)
+    assert G.caches_equal(hk[idx_d], k0[idx_s]) and G.caches_equal(hv[idx_d], v0[idx_s])
+    rest = torch.from_numpy(np.setdiff1d(np.arange(24), dst))
+    assert torch.isnan(hk[rest].float()).all() and torch.isnan(hv[rest].float()).all()
+    # swap back in to other device blocks
+    back = rng.choice(40, 12, replace=False)
+    in_pairs = torch.from_numpy(np.stack([dst, back], 1).astype(np.int32)).cuda()
+    kc2, vc2 = torch.zeros_like(kc), torch.zeros_like(vc)
+    pa.swap_blocks(kc2, vc2, hk, hv, in_pairs)
+    torch.cuda.synchronize()
+    idx_b = torch.from_numpy(back).cuda()
+    assert G.caches_equal(kc2[idx_b], kc[torch.from_numpy(src).cuda()])
+    assert G.caches_equal(vc2[idx_b], vc[torch.from_numpy(src).cuda()])
+    untouched = torch.from_numpy(np.setdiff1d(np.arange(40), back)).cuda()
+    assert int(kc2[untouched].abs().sum().item()) == 0 and int(vc2[untouched].abs().sum().item()) == 0
