@@ -152,3 +152,49 @@ def test_prefix_cache_mutants_are_caught(monkeypatch):
         mp.setattr(PC.PrefixCacheModel, "match", match_without_refs)
         with pytest.raises(AssertionError):
             TP.test_page_example_block_table()
+
+
+def _top_left_positions(n, L):
+    return np.arange(n, dtype=np.int64)          # mask not shifted to the end
+
+
+def _late_positions(n, L):
+    return np.arange(n, dtype=np.int64) + (L - n) + 1
+
+
+def _strict_causal(Q, K, V, pos, scale):
+    return _real_causal(Q, K, V, pos - 1, scale)  # a row misses its own key
+
+
+def _unmasked(Q, K, V, pos, scale):
+    return _real_causal(Q, K, V, np.full_like(pos, K.shape[0]), scale)
+
+
+from oracle import prefill as PF  # noqa: E402
+from tests import test_oracle_prefill as TPF  # noqa: E402
+
+_real_causal = PF.causal_attend
+
+
+@pytest.mark.parametrize("attr,mutant", [
+    ("row_positions", _top_left_positions),
+    ("row_positions", _late_positions),
+    ("causal_attend", _strict_causal),
+    ("causal_attend", _unmasked),
+])
+def test_prefill_mutants_are_caught(monkeypatch, attr, mutant):
+    """Each planted mask mistake fails at least one prefill pin."""
+    pins = [TPF.test_chunk_matches_sdpa_end_aligned_mask,
+            lambda: TPF.test_whole_prompt_matches_sdpa_causal(8, 2),
+            TPF.test_first_row_is_first_value,
+            TPF.test_one_new_token_is_decode]
+    for pin in pins:
+        pin()
+    monkeypatch.setattr(PF, attr, mutant)
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failed += 1
+    assert failed >= 1
