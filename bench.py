@@ -195,6 +195,196 @@ def bench_swap(args) -> int:
     return 0
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # dense f16 / bf16 matrix cores
+
+
+def prefill_flops(rows, seq_lens, Hq: int, D: int) -> int:
+    """Algorithmic flops of causal prefill: per query row and head, q.k over
+    the pos + 1 keys it sees (2 D flops each) and p.v over the same keys
+    (2 D each); masked-out keys count nothing."""
+    import numpy as np
+
+    total = 0
+    qsl = rows.query_start_loc
+    for b in range(len(seq_lens)):
+        n, L = int(qsl[b + 1] - qsl[b]), int(seq_lens[b])
+        pos = np.arange(n, dtype=np.int64) + (L - n)
+        total += int(np.maximum(pos + 1, 0).sum())
+    return 4 * D * Hq * total
+
+
+def cpu_baseline_prefill(wl, rows, seconds: float):
+    """The prefill oracle, unchanged, on evenly spaced rows of the first
+    sequence (all query heads), the row count grown until the time budget
+    is spent."""
+    import numpy as np
+    import torch
+
+    from oracle import cache_write as OW
+    from oracle import prefill as OP
+    from synth.generate import empty_cache_cpu
+
+    kc, vc = empty_cache_cpu(wl), empty_cache_cpu(wl)
+    OW.reshape_and_cache(wl.tok_key, wl.tok_value, wl.slot_mapping, kc, vc,
+                         wl.cfg.kv_dtype, wl.k_scale, wl.v_scale)
+    c = wl.cfg
+    n0 = int(rows.query_start_loc[1])
+    L0 = int(wl.seq_lens[0])
+    q0 = rows.query[:n0]
+    count, used, flops = 16, 0.0, 0
+    while True:
+        sel = np.unique(np.linspace(0, n0 - 1, min(count, n0)).astype(np.int64))
+        t0 = time.perf_counter()
+        OP.paged_prefill_stored(q0, kc, vc, c.kv_dtype, wl.k_scale, wl.v_scale,
+                                wl.block_tables[:1], wl.seq_lens[:1], np.array([0, n0]),
+                                wl.scale, c.block_size, rows=sel)
+        used = time.perf_counter() - t0
+        pos = sel + (L0 - n0)
+        flops = 4 * c.head_dim * c.num_q_heads * int((pos + 1).sum())
+        if used >= seconds / 3 or len(sel) >= n0:
+            break
+        count *= 4
+    return {
+        "value": round(flops / used / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(torch.get_num_threads()),
+        "kind": "oracle",
+        "sample": f"fp64 prefill oracle on {len(sel)} evenly spaced rows of sequence 0 "
+                  f"({n0} rows, {L0} tokens), all {c.num_q_heads} query heads, "
+                  f"{flops / 1e9:.2f} GFLOP in {used:.2f} s",
+    }
+
+
+def bench_prefill(args) -> int:
+    """One step = write the new tokens' K/V into the cache
+    (pa_reshape_and_cache) and take causal attention of their query rows
+    over the cache (pa_prefill).  The prefill launch is timed with HIP
+    events on the launch stream; its algorithmic flops against the dense
+    16-bit MFMA peak."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_462_amd as pa
+    from synth import get_prefill_config, make_prefill_rows, make_workload
+
+    name = args.config if not args.config.startswith("c") else "p1"
+    cfg, news = get_prefill_config(name)
+    log(f"[bench] generating {cfg.name}")
+    wl = make_workload(cfg)
+    rows = make_prefill_rows(wl, news)
+    c = wl.cfg
+    dev = torch.device("cuda:0")
+    fp8 = c.kv_dtype == "fp8"
+    kvd = "fp8" if fp8 else None
+    shape = (wl.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    st = torch.uint8 if fp8 else wl.tok_key.dtype
+    kc = torch.zeros(shape, dtype=st, device=dev)
+    vc = torch.zeros(shape, dtype=st, device=dev)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.seq_lens).to(dev)
+    qsl = torch.from_numpy(rows.query_start_loc).to(dev)
+    q = rows.query.to(dev)
+    out = torch.empty_like(q)
+    # the new tokens' K/V: the last n_b of each sequence in the token stream
+    starts = np.concatenate([[0], np.cumsum(wl.seq_lens.astype(np.int64))])
+    if cfg.shared_prefix_tokens:
+        raise SystemExit("prefill workloads take no shared prefix")
+    new_idx = np.concatenate([np.arange(starts[b + 1] - rows.new_tokens[b], starts[b + 1])
+                              for b in range(c.batch)]).astype(np.int64)
+    tok_k = wl.tok_key.to(dev)
+    tok_v = wl.tok_value.to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    pa.reshape_and_cache(tok_k, tok_v, slots, kc, vc, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                         kv_dtype=kvd)
+    ni = torch.from_numpy(new_idx).to(dev)
+    new_k, new_v, new_s = tok_k[ni].contiguous(), tok_v[ni].contiguous(), slots[ni].contiguous()
+    del tok_k, tok_v
+    # calibration copy for the FETCH_SIZE / WRITE_SIZE counters
+    cal_src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
+    mq = rows.max_query_len
+    stream = torch.cuda.current_stream()
+
+    def step_write():
+        pa.reshape_and_cache(new_k, new_v, new_s, kc, vc, k_scale=wl.k_scale,
+                             v_scale=wl.v_scale, kv_dtype=kvd)
+
+    def step_attn():
+        pa.prefill(out, q, kc, vc, tables, lens, qsl, mq, wl.scale, c.block_size,
+                   c.num_kv_heads, k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
+
+    for _ in range(args.warmup):
+        step_write()
+        step_attn()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    log(f"[bench] timing {K} prefill steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        step_write()
+        evs[i][0].record(stream)
+        step_attn()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    att_ms = [a.elapsed_time(b) for a, b in evs]
+    att_mean = float(np.mean(att_ms))
+    flops = prefill_flops(rows, wl.seq_lens, c.num_q_heads, c.head_dim)
+    achieved = flops / (att_mean * 1e-3) / 1e12
+    res = {
+        "metric": "paged causal prefill attention: TFLOP/s (algorithmic, unmasked part) and tokens/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.q_dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": c.name,
+            "batch": c.batch,
+            "num_q_heads": c.num_q_heads,
+            "num_kv_heads": c.num_kv_heads,
+            "head_dim": c.head_dim,
+            "block_size": c.block_size,
+            "seq_lens": list(map(str, c.lengths)),
+            "new_tokens": list(map(str, news)),
+            "query_rows": rows.num_rows,
+            "q_dtype": c.q_dtype,
+            "kv_dtype": c.kv_dtype,
+            "flops_per_step": flops,
+            "parallelism": "single GPU",
+        },
+        "tokens_per_s": round(rows.num_rows / (ms_step * 1e-3), 1),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "pa_prefill",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "mean_launch_ms": round(att_mean, 5),
+            "median_launch_ms": round(float(np.median(att_ms)), 5),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_seconds}s)")
+        res["cpu_baseline"] = cpu_baseline_prefill(wl, rows, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -208,9 +398,10 @@ def main() -> int:
     ap.add_argument("--hot-iters", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", default="decode", choices=["decode", "swap"],
-                    help="decode: the decode hot path (default); swap: the batch's KV blocks "
-                         "swapped out to pinned host memory and back in (pa_swap_blocks)")
+    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "swap"],
+                    help="decode: the decode hot path (default); prefill: causal prefill of "
+                         "new tokens over the cache (--config p1 | p2); swap: the batch's KV "
+                         "blocks swapped out to pinned host memory and back in (pa_swap_blocks)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -232,6 +423,8 @@ def main() -> int:
     pa.load()
     if args.op == "swap":
         return bench_swap(args)
+    if args.op == "prefill":
+        return bench_prefill(args)
     cfg = get_config(args.config)
     log(f"[bench] generating {cfg.name}")
     wl = make_workload(cfg)

@@ -144,6 +144,49 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
               const pa_launch* launch);
 
 /*
+ * pa_prefill -- causal attention of a batch of new tokens over the paged
+ * cache ("5.KV Cache 管理 & PagedAttention", question 6, `MHAWithCache`
+ * prefill branch, lower-triangular mask; question 19, query tiles against
+ * the logical KV blocks of the block table with an online softmax;
+ * question 3, section 3.3, prefill K/V kept in the cache).  Sequence b has
+ * seq_lens[b] tokens in the cache, the new ones included (write them with
+ * pa_reshape_and_cache first); its n_b = query_start_loc[b+1] -
+ * query_start_loc[b] query rows are its last n_b tokens, so row i sits at
+ * position p = seq_lens[b] - n_b + i and
+ *   out[row, h] = softmax(scale * q[row, h] . K_b[0..p]^T) V_b[0..p]
+ * with kv head h / (Hq / Hkv).  n_b == seq_lens[b] is a whole prompt;
+ * n_b < seq_lens[b] continues a sequence whose earlier tokens are cached
+ * (a chunked prompt, or a prefix shared through the prefix cache).  A row
+ * whose position would be negative (n_b > seq_lens[b]) attends no token and
+ * gets zeros.
+ *   out             [T, Hq, D]    dtype of query; dim stride 1; rows 16-byte
+ *                                 aligned (like the query's)
+ *   query           [T, Hq, D]    f16 | bf16; dim stride 1; the rows of all
+ *                                 sequences back to back
+ *   key_cache,
+ *   value_cache     [N, bs, Hkv, D] contiguous; dtype of query, or
+ *                                 PA_FP8_E4M3 with per-tensor `scale`
+ *   block_tables    [B, max_blocks] i32, column stride 1; entries past
+ *                                 ceil(seq_lens[b] / bs) are never read
+ *   seq_lens        [B] i32, 0 <= seq_lens[b] <= max_blocks * bs
+ *   query_start_loc [B + 1] i32 (device), query_start_loc[0] = 0, rising to
+ *                                 query_start_loc[B] = T
+ *   max_query_len   an upper bound of every n_b (sizes the grid; a smaller
+ *                   value is still correct, only slower); <= 0 uses T
+ *   scale, block_size (a multiple of 16), num_kv_heads: as for pa_decode
+ *   launch          stream (workspace and partitioning unused); NULL = null
+ *                   stream
+ * Supported head_dim: 128.  No workspace; deterministic.  Asynchronous on
+ * launch->stream.
+ */
+int pa_prefill(pa_tensor* out, const pa_tensor* query,
+               const pa_tensor* key_cache, const pa_tensor* value_cache,
+               const pa_tensor* block_tables, const pa_tensor* seq_lens,
+               const pa_tensor* query_start_loc, int32_t max_query_len,
+               float scale, int32_t block_size, int32_t num_kv_heads,
+               const pa_launch* launch);
+
+/*
  * pa_copy_blocks -- device copy of whole physical blocks, the data step of
  * copy-on-write ("5.KV Cache 管理 & PagedAttention", question 18,
  * copy_block): for each row (src, dst) of block_pairs,

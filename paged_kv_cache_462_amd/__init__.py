@@ -1,4 +1,4 @@
-"""MI355X (gfx950) paged decode attention.
+"""MI355X (gfx950) attention over a paged KV cache: decode and prefill.
 
 The compute lives in libpa.so (hand-written HIP kernels behind a C ABI,
 declared in include/pa.h).  This package is a thin binding: it marshals torch
@@ -19,6 +19,7 @@ from .ops import (  # noqa: F401
     decode,
     decode_plan,
     decode_workspace_bytes,
+    prefill,
     reshape_and_cache,
     swap_blocks,
 )

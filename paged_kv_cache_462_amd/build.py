@@ -28,7 +28,8 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
-SOURCES = ["pa_decode.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_alloc.cpp", "pa_prefix.cpp"]
+SOURCES = ["pa_decode.hip", "pa_prefill.hip", "pa_cache_write.hip", "pa_api.cpp", "pa_alloc.cpp",
+           "pa_prefix.cpp"]
 
 
 def _compile(src: str) -> str:

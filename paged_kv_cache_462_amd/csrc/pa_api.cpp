@@ -12,6 +12,7 @@
 
 #include "../../include/pa.h"
 #include "pa_internal.h"
+#include "pa_prefill.h"
 
 namespace {
 
@@ -150,7 +151,8 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 const char* pa_build_info(void) {
   return "target gfx950 (CDNA4); decode VALU {f32,f16,bf16,fp8-kv} x head_dim {64,128} x "
          "heads/tile {1,2,4}; decode MFMA {f16,bf16,fp8-kv} x head_dim {64,128} x 16 heads/tile; "
-         "split-partition merge; cache write {copy, fp8 e4m3 quantise}; block copy";
+         "split-partition merge; prefill MFMA {f16,bf16} x {same,fp8} kv x head_dim 128; "
+         "cache write {copy, fp8 e4m3 quantise}; block copy";
 }
 
 int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -349,6 +351,95 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value, const pa_
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_cache_write(p, kind_of(sdt), kind_of(cdt), stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache write launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+               const pa_tensor* value_cache, const pa_tensor* block_tables,
+               const pa_tensor* seq_lens, const pa_tensor* query_start_loc,
+               int32_t max_query_len, float scale, int32_t block_size, int32_t num_kv_heads,
+               const pa_launch* launch) {
+  int rc;
+  if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(out, "out", 3)) ||
+      (rc = check_cache_pair(key_cache, value_cache)) ||
+      (rc = check_tensor(block_tables, "block_tables", 2)) ||
+      (rc = check_tensor(seq_lens, "seq_lens", 1)) ||
+      (rc = check_tensor(query_start_loc, "query_start_loc", 1)))
+    return rc;
+  const int qdt = query->dtype;
+  if (qdt != PA_F16 && qdt != PA_BF16) return fail(PA_ERR_INVALID_ARG, "query dtype must be f16 or bf16");
+  if (out->dtype != qdt) return fail(PA_ERR_INVALID_ARG, "out dtype must equal the query dtype");
+  const int64_t T = query->shape[0], Hq = query->shape[1], D = query->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != query->shape[i]) return fail(PA_ERR_INVALID_ARG, "out shape must equal the query shape");
+  if (query->stride[2] != 1 || out->stride[2] != 1)
+    return fail(PA_ERR_INVALID_ARG, "query/out head_dim stride must be 1");
+  const int64_t N = key_cache->shape[0], bs = key_cache->shape[1], Hkv = key_cache->shape[2];
+  if (key_cache->shape[3] != D) return fail(PA_ERR_INVALID_ARG, "cache head_dim %lld != query head_dim %lld",
+                                            (long long)key_cache->shape[3], (long long)D);
+  if (bs != block_size) return fail(PA_ERR_INVALID_ARG, "block_size %d != cache block dimension %lld",
+                                    block_size, (long long)bs);
+  if (Hkv != num_kv_heads) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d != cache head dimension %lld",
+                                       num_kv_heads, (long long)Hkv);
+  if (Hkv <= 0 || Hq % Hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  if (bs % 16) return fail(PA_ERR_UNSUPPORTED, "block_size must be a multiple of 16 (got %lld)", (long long)bs);
+  const int kvdt = key_cache->dtype;
+  if (kvdt != qdt && kvdt != PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID_ARG, "cache dtype must equal the query dtype, or be fp8");
+  if (block_tables->dtype != PA_I32 || seq_lens->dtype != PA_I32 || query_start_loc->dtype != PA_I32)
+    return fail(PA_ERR_INVALID_ARG, "block_tables, seq_lens and query_start_loc must be int32");
+  const int64_t B = seq_lens->shape[0];
+  if (block_tables->shape[0] != B || query_start_loc->shape[0] != B + 1)
+    return fail(PA_ERR_INVALID_ARG, "block_tables [B, .] and query_start_loc [B + 1] must match seq_lens [B]");
+  if (block_tables->stride[1] != 1 || (seq_lens->stride[0] != 1 && B > 1) || query_start_loc->stride[0] != 1)
+    return fail(PA_ERR_INVALID_ARG, "block_tables column stride, seq_lens and query_start_loc strides must be 1");
+  if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "batch above 65535");
+  if (Hq > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 query heads");
+  if (T > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || block_tables->shape[1] > 0x7FFFFFFFLL)
+    return fail(PA_ERR_UNSUPPORTED, "rows, pool or table too large");
+  if ((int64_t)block_tables->shape[1] * bs > (1LL << 30))
+    return fail(PA_ERR_INVALID_ARG, "block table addresses too many tokens");
+  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  const int64_t vec = 8;  // 16-bit elements per 16 bytes
+  if (!aligned16(query->data) || query->stride[0] % vec || query->stride[1] % vec)
+    return fail(PA_ERR_INVALID_ARG, "query rows must be 16-byte aligned");
+  if (!aligned16(out->data) || out->stride[0] % vec || out->stride[1] % vec)
+    return fail(PA_ERR_INVALID_ARG, "out rows must be 16-byte aligned");
+  if (!pa::prefill_variant_built(kind_of(qdt), kind_of(kvdt), (int)D))
+    return fail(PA_ERR_UNSUPPORTED, "no prefill variant for this dtype / head_dim (head_dim 128 is built)");
+  if (B == 0 || T == 0 || Hq == 0) return PA_OK;
+
+  const int64_t bm = pa::prefill_rows_per_workgroup();
+  const int64_t mq = max_query_len > 0 && max_query_len < T ? max_query_len : T;
+  int64_t ranks = (mq + bm - 1) / bm;
+  if (ranks * B > 65535) ranks = 65535 / B;  // the kernel loops over the rest
+  pa::PrefillParams p;
+  memset(&p, 0, sizeof p);
+  p.out = out->data;
+  p.q = query->data;
+  p.kc = key_cache->data;
+  p.vc = value_cache->data;
+  p.tables = static_cast<const int32_t*>(block_tables->data);
+  p.lens = static_cast<const int32_t*>(seq_lens->data);
+  p.qsl = static_cast<const int32_t*>(query_start_loc->data);
+  p.q_st = query->stride[0];
+  p.q_sh = query->stride[1];
+  p.o_st = out->stride[0];
+  p.o_sh = out->stride[1];
+  p.tab_stride = block_tables->stride[0];
+  p.B = (int)B;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.G = (int)(Hq / Hkv);
+  p.D = (int)D;
+  p.bs = (int)bs;
+  p.tile_ranks = (int)ranks;
+  const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
+  p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
+  p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
+  hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  hipError_t e = pa::launch_prefill(p, kind_of(qdt), kind_of(kvdt), stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

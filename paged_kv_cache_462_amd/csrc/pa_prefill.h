@@ -1,0 +1,36 @@
+// Internal interface of the paged prefill kernel (pa_prefill.hip) for the
+// C-ABI layer.  Host code only; no torch types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything the prefill kernel reads, resolved on the host.
+struct PrefillParams {
+  void* out;              // [T, Hq, D] query dtype
+  const void* q;          // [T, Hq, D]
+  const void* kc;         // [N, bs, Hkv, D]
+  const void* vc;
+  const int32_t* tables;  // [B, tab_stride]
+  const int32_t* lens;    // [B] tokens in the cache, new ones included
+  const int32_t* qsl;     // [B + 1] first packed row of each sequence
+  int64_t q_st, q_sh;     // query strides (elements): token, head
+  int64_t o_st, o_sh;     // output strides
+  int64_t tab_stride;     // block-table row stride
+  int32_t B, Hq, Hkv, G, D, bs;
+  int32_t tile_ranks;     // query-tile ranks in the grid (grid.y / B)
+  float qk_scale_log2;    // scale * k_scale * log2(e)
+  float v_scale;          // fp8 V scale (1 otherwise)
+};
+
+// Query rows one workgroup takes.
+int prefill_rows_per_workgroup();
+
+// hipErrorNotSupported when no built variant matches (qkind, kvkind, D).
+hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream);
+
+bool prefill_variant_built(int qkind, int kvkind, int D);
+
+}  // namespace pa

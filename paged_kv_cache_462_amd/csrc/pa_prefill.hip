@@ -1,0 +1,320 @@
+// Paged prefill attention for gfx950 (CDNA4).
+//
+// The method: a batch of new tokens per sequence, whose K/V are already in
+// the paged cache, attends causally over the sequence's cached tokens.  The
+// rows of a sequence are its last n tokens; the row at position p sees the
+// tokens at positions 0..p ("5.KV Cache 管理 & PagedAttention", question 6,
+// `MHAWithCache` prefill branch: lower-triangular mask; question 19: outer
+// loop over query tiles, inner loop over the logical KV blocks looked up in
+// the block table, online softmax, normalise at the end; question 3,
+// section 3.3: the prefill pass keeps its K/V in the cache).  With a few
+// hundred query rows per tile this is a dense contraction, so both products
+// run on the matrix cores.
+//
+// Work decomposition.  A workgroup is four waves and takes one query head
+// and one tile of kBM consecutive rows of one sequence; each wave owns
+// kQSub 16-row subtiles.  The grid is (query head, tile rank x sequence):
+// rank 0 is the last (heaviest, it sees the most keys) tile of every
+// sequence, so the long tiles are dispatched first and the short ones fill
+// in at the end.  A workgroup walks the keys the tile needs, 64 at a time:
+//  * the four 16-token subtiles of a 64-key tile each lie inside one
+//    physical block (the block size is a multiple of 16), so their block
+//    ids are workgroup-uniform scalar loads from the table;
+//  * every thread loads four 16-byte chunks of K and of V rows (16 lanes
+//    per 256-byte row) into registers one tile ahead and writes them to a
+//    double-buffered LDS tile after the current tile's compute; K rows
+//    go in with an XOR swizzle of their 16-byte chunks so that the score
+//    operand reads (16 rows, one chunk) hit 16 different bank groups.
+// Per wave and KV tile:
+//  * scores^T[16 keys x 16 rows] = K[16 x D] . Q^T[D x 16] on
+//    v_mfma_f32_16x16x32; Q stays in registers for the whole tile.  Lane l
+//    gets keys 4*(l/16)+i of query row l%16;
+//  * online softmax per row in the exp2 domain (the score scale carries
+//    log2 e): the row max over the 64 keys needs two cross-lane steps (the
+//    four lanes l, l^16, l^32, l^48 share a row); the running sum stays
+//    per lane and is combined once at the end;
+//  * out^T[D x 16] += V^T[D x 32 keys] . P^T[32 keys x 16] on
+//    v_mfma_f32_16x16x32: the k index of that product runs over keys in
+//    the order the score tile left them in the lanes (keys 4g..4g+3 and
+//    16+4g..16+4g+3 for lane group g), so P^T needs no data movement; the
+//    V^T operand takes element j of 8 LDS rows (MFMA j, row m computes
+//    dim 8m + j), packed with v_perm;
+//  * bf16 P is split into a high and a low bf16 part, each with its own
+//    P.V product, so that the weights keep ~16 significant bits (a single
+//    bf16 P uses most of the error budget of a 16-bit result).
+// Causal masking only touches the KV tiles that cross the wave's diagonal.
+#include "pa_device.h"
+#include "pa_internal.h"
+#include "pa_prefill.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBN = 64;                      // keys per KV tile
+constexpr int kQSub = 4;                     // 16-row query subtiles per wave
+constexpr int kBM = kWaves * kQSub * 16;     // query rows per workgroup
+
+template <int KIND>
+struct Esz {
+  static constexpr int v = KIND == K_FP8 ? 1 : 2;
+};
+
+// 16 bytes of one K/V row chunk (8 elements) as 16-bit MFMA input.
+template <int KVK, bool BF>
+__device__ __forceinline__ i32x4 load_chunk(const char* p) {
+  if constexpr (KVK == K_FP8) {
+    const i32x2 raw = *reinterpret_cast<const i32x2*>(p);
+    const i32x2 lo = BF ? fp8x4_to_bf16x4((uint32_t)raw[0]) : fp8x4_to_f16x4((uint32_t)raw[0]);
+    const i32x2 hi = BF ? fp8x4_to_bf16x4((uint32_t)raw[1]) : fp8x4_to_f16x4((uint32_t)raw[1]);
+    return i32x4{lo[0], lo[1], hi[0], hi[1]};
+  } else {
+    return *reinterpret_cast<const i32x4*>(p);
+  }
+}
+
+template <int QK, int KVK, int D>
+__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
+  static_assert(D == 128, "one 16-byte chunk per lane of a 16-lane row");
+  constexpr bool BF = QK == K_BF16;
+  constexpr int C = D / 8;      // 16-bit chunks of 8 elements per row
+  constexpr int KS = D / 32;    // k-steps of the score product
+  constexpr int ESZ = Esz<KVK>::v;
+  __shared__ i32x4 k_lds[2][kBN * C];
+  __shared__ i32x4 v_lds[2][kBN * C];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+  const int h = blockIdx.x;
+  const int b = blockIdx.y % p.B;
+  const int rank = blockIdx.y / p.B;
+  const int kvh = h / p.G;
+  const int q0 = p.qsl[b];
+  const int n = p.qsl[b + 1] - q0;
+  const int L = p.lens[b];
+  const int ntiles = (n + kBM - 1) / kBM;
+  const int ctx = L - n;  // position of row 0 (negative when n > L)
+  const int32_t* tab = p.tables + (int64_t)b * p.tab_stride;
+  const int64_t tok_bytes = (int64_t)p.Hkv * D * ESZ;
+  const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
+  const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
+  // staging: thread -> row srow + 16 i of the KV tile, chunk sch
+  const int srow = threadIdx.x >> 4;
+  const int sch = threadIdx.x & 15;
+
+  for (int tile = ntiles - 1 - rank; tile >= 0; tile -= p.tile_ranks) {
+    const int row0 = tile * kBM;
+    const int rows = min(kBM, n - row0);
+    const int kv_end = min(L, ctx + row0 + rows);  // keys [0, kv_end)
+    const int ntk = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
+    const int wrow0 = row0 + w * kQSub * 16;
+    const int wrows = max(0, min(kQSub * 16, n - wrow0));
+    const int w_end = wrows > 0 ? min(L, ctx + wrow0 + wrows) : 0;
+    const int w_first = ctx + wrow0;
+
+    i32x4 qf[kQSub][KS];
+    int pos[kQSub];
+#pragma unroll
+    for (int qs = 0; qs < kQSub; ++qs) {
+      const int row = wrow0 + qs * 16 + n16;
+      const int rc = min(row, n - 1);
+      pos[qs] = ctx + row;
+      const char* qp = static_cast<const char*>(p.q) + ((int64_t)(q0 + rc) * p.q_st + (int64_t)h * p.q_sh) * 2;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) qf[qs][st] = *reinterpret_cast<const i32x4*>(qp + (4 * st + g) * 16);
+    }
+    float m[kQSub], l[kQSub];
+    f32x4 o[kQSub][8];
+#pragma unroll
+    for (int qs = 0; qs < kQSub; ++qs) {
+      m[qs] = kMaxFloor;
+      l[qs] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[qs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    i32x4 kr[4], vr[4];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sub0 = kt * kBN + 16 * i;  // workgroup-uniform
+        kr[i] = i32x4{0, 0, 0, 0};
+        vr[i] = i32x4{0, 0, 0, 0};
+        if (sub0 < L) {
+          const int tok = sub0 + srow;
+          const int blk = tab[sub0 / p.bs];
+          const int64_t off = ((int64_t)blk * p.bs + tok % p.bs) * tok_bytes + sch * 8 * ESZ;
+          const i32x4 kx = load_chunk<KVK, BF>(kbase + off);
+          const i32x4 vx = load_chunk<KVK, BF>(vbase + off);
+          // slots past the sequence's end hold stale data: zero them
+          const bool live = tok < L;
+          kr[i] = live ? kx : i32x4{0, 0, 0, 0};
+          vr[i] = live ? vx : i32x4{0, 0, 0, 0};
+        }
+      }
+    };
+
+    __syncthreads();  // the previous tile's last KV tile is no longer read
+    if (ntk > 0) load_tile(0);
+    for (int kt = 0; kt < ntk; ++kt) {
+      const int buf = kt & 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = srow + 16 * i;
+        k_lds[buf][r * C + (sch ^ srow)] = kr[i];
+        v_lds[buf][r * C + sch] = vr[i];
+      }
+      __syncthreads();
+      if (kt + 1 < ntk) load_tile(kt + 1);
+
+      const int key0 = kt * kBN;
+      if (key0 >= w_end) continue;  // every row of this wave is done
+      const bool need_mask = key0 + kBN - 1 > w_first;
+
+      // scores^T for the 4 key subtiles x kQSub row subtiles
+      f32x4 s[kQSub][4];
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) s[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int r = ks * 16 + n16;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) {
+          const i32x4 kf = k_lds[buf][r * C + ((4 * st + g) ^ n16)];
+#pragma unroll
+          for (int qs = 0; qs < kQSub; ++qs) s[qs][ks] = mfma_k32<BF>(kf, qf[qs][st], s[qs][ks]);
+        }
+      }
+
+      // online softmax; P^T operands (keys 4g+e of subtiles 2s2 and 2s2+1)
+      i32x4 ph[kQSub][2], pl[kQSub][2];
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs) {
+        float x[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = s[qs][ks][e] * p.qk_scale_log2;
+            if (need_mask) v = key0 + ks * 16 + 4 * g + e <= pos[qs] ? v : -INFINITY;
+            x[ks][e] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mn = fmaxf(m[qs], tmax);
+        const float alpha = fast_exp2(m[qs] - mn);
+        m[qs] = mn;
+        float sum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[ks][e] = fast_exp2(x[ks][e] - mn);
+            sum += x[ks][e];
+          }
+        l[qs] = l[qs] * alpha + sum;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[qs][j] *= alpha;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float* a = x[2 * s2];
+          const float* c = x[2 * s2 + 1];
+          if constexpr (BF) {
+            const uint32_t h0 = pack_bf16(a[0], a[1]), h1 = pack_bf16(a[2], a[3]);
+            const uint32_t h2 = pack_bf16(c[0], c[1]), h3 = pack_bf16(c[2], c[3]);
+            ph[qs][s2] = i32x4{(int)h0, (int)h1, (int)h2, (int)h3};
+            pl[qs][s2] = i32x4{(int)pack_bf16(a[0] - bf16_lo(h0), a[1] - bf16_hi(h0)),
+                               (int)pack_bf16(a[2] - bf16_lo(h1), a[3] - bf16_hi(h1)),
+                               (int)pack_bf16(c[0] - bf16_lo(h2), c[1] - bf16_hi(h2)),
+                               (int)pack_bf16(c[2] - bf16_lo(h3), c[3] - bf16_hi(h3))};
+          } else {
+            ph[qs][s2] = i32x4{(int)pack_f16(a[0], a[1]), (int)pack_f16(a[2], a[3]),
+                               (int)pack_f16(c[0], c[1]), (int)pack_f16(c[2], c[3])};
+          }
+        }
+      }
+
+      // out^T += V^T . P^T, 32 keys per step
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        i32x4 vw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = s2 * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
+          vw[e] = v_lds[buf][key * C + n16];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int dw = j >> 1;
+          i32x4 a;
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr)
+            a[pr] = (int)((j & 1) ? pack_hi_halves((uint32_t)vw[2 * pr][dw], (uint32_t)vw[2 * pr + 1][dw])
+                                  : pack_lo_halves((uint32_t)vw[2 * pr][dw], (uint32_t)vw[2 * pr + 1][dw]));
+#pragma unroll
+          for (int qs = 0; qs < kQSub; ++qs) {
+            o[qs][j] = mfma_k32<BF>(a, ph[qs][s2], o[qs][j]);
+            if constexpr (BF) o[qs][j] = mfma_k32<BF>(a, pl[qs][s2], o[qs][j]);
+          }
+        }
+      }
+    }
+
+    // normalise and store: lane holds dims 32g .. 32g+31 of its row
+#pragma unroll
+    for (int qs = 0; qs < kQSub; ++qs) {
+      float lt = l[qs];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
+      const int row = wrow0 + qs * 16 + n16;
+      if (row < n) {
+        char* op = static_cast<char*>(p.out) + ((int64_t)(q0 + row) * p.o_st + (int64_t)h * p.o_sh + 32 * g) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          i32x4 v;
+#pragma unroll
+          for (int pr = 0; pr < 4; ++pr) {
+            const float a0 = o[qs][2 * pr][i] * inv, a1 = o[qs][2 * pr + 1][i] * inv;
+            v[pr] = (int)(BF ? pack_bf16(a0, a1) : pack_f16(a0, a1));
+          }
+          *reinterpret_cast<i32x4*>(op + i * 16) = v;
+        }
+      }
+    }
+  }
+}
+
+template <int QK, int KVK, int D>
+hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)p.Hq, (unsigned)(p.tile_ranks * p.B));
+  hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int prefill_rows_per_workgroup() { return kBM; }
+
+bool prefill_variant_built(int qkind, int kvkind, int D) {
+  if (D != 128) return false;
+  if (qkind != K_F16 && qkind != K_BF16) return false;
+  return kvkind == qkind || kvkind == K_FP8;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
+  if (!prefill_variant_built(qkind, kvkind, p.D)) return hipErrorNotSupported;
+  if (qkind == K_F16)
+    return kvkind == K_FP8 ? launch_one<K_F16, K_FP8, 128>(p, stream) : launch_one<K_F16, K_F16, 128>(p, stream);
+  return kvkind == K_FP8 ? launch_one<K_BF16, K_FP8, 128>(p, stream) : launch_one<K_BF16, K_BF16, 128>(p, stream);
+}
+
+}  // namespace pa

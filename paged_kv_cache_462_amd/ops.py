@@ -127,6 +127,24 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                            int(block_size), int(num_kv_heads), byref(ln)))
 
 
+def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+            value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+            query_start_loc: torch.Tensor, max_query_len: int, scale: float, block_size: int,
+            num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0,
+            kv_dtype: Optional[str] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_prefill: causal attention of the packed new rows of every sequence
+    over its cached tokens (the new tokens' K/V already written)."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
+            _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
+            _desc(query_start_loc))
+    ln = _launch(query, None, 0, PATH_AUTO, stream)
+    check(load().pa_prefill(*(byref(a) for a in args), int(max_query_len),
+                            ctypes.c_float(scale), int(block_size), int(num_kv_heads),
+                            byref(ln)))
+
+
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,
                 kv_dtype: Optional[str] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
     """pa_copy_blocks: key/value_cache[dst] = key/value_cache[src] per pair."""

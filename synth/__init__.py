@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for paged decode attention.
+"""Seeded synthetic inputs for paged decode and prefill attention.
 
 This package only draws inputs: sequence lengths, physical block ids, block
 tables, queries and the K/V token stream that fills the cache.  It holds none
@@ -6,5 +6,6 @@ of the method's arithmetic (no gather, no softmax, no quantisation); both the
 CPU oracle and the HIP path consume what it produces.
 """
 
-from .configs import CONFIGS, WorkloadConfig, get_config  # noqa: F401
-from .generate import Workload, make_workload  # noqa: F401
+from .configs import (CONFIGS, PREFILL_CONFIGS, WorkloadConfig, get_config,  # noqa: F401
+                      get_prefill_config)
+from .generate import PrefillRows, Workload, make_prefill_rows, make_workload  # noqa: F401

@@ -97,6 +97,37 @@ _add(WorkloadConfig(
 # Ordered as listed above; index 0 is the small case, index 1 the bench case.
 CONFIG_ORDER = list(CONFIGS)
 
+# Prefill workloads: the cache holds each sequence's tokens (drawn as for
+# decode); a prefill call brings the last `new_tokens` of them as query rows
+# (synth.generate.make_prefill_rows).  Same model shapes as above.
+PREFILL_CONFIGS: Dict[str, Tuple[WorkloadConfig, Tuple]] = {}
+
+
+def _add_prefill(c: WorkloadConfig, new_tokens: Tuple) -> None:
+    PREFILL_CONFIGS[c.name] = (c, new_tokens)
+
+
+_add_prefill(WorkloadConfig(
+    name="llama2_7b_prefill_fp16",
+    description="8 prompts of 2048 tokens, whole-prompt causal prefill, "
+                "32 q = 32 kv heads, d=128, bs=16, fp16",
+    batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128, block_size=16,
+    q_dtype="f16", kv_dtype="f16", lengths=("fixed", 2048), seed=2001), ("all",))
+
+_add_prefill(WorkloadConfig(
+    name="llama2_70b_gqa_chunked_prefill_bf16",
+    description="4 sequences of 4096 tokens, the last 1024 as one prefill "
+                "chunk over 3072 cached tokens, 64 q / 8 kv heads, d=128, "
+                "bs=16, bf16",
+    batch=4, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+    q_dtype="bf16", kv_dtype="bf16", lengths=("fixed", 4096), seed=2002),
+    ("fixed", 1024))
+
+
+def get_prefill_config(name: str) -> Tuple[WorkloadConfig, Tuple]:
+    aliases = {f"p{i + 1}": n for i, n in enumerate(PREFILL_CONFIGS)}
+    return PREFILL_CONFIGS[aliases.get(name, name)]
+
 
 def get_config(name_or_index) -> WorkloadConfig:
     if isinstance(name_or_index, int):

@@ -217,6 +217,48 @@ def empty_cache_cpu(wl: Workload) -> torch.Tensor:
     return torch.full(shape, float("nan"), dtype=TORCH_DTYPES[c.kv_dtype])
 
 
+@dataclass
+class PrefillRows:
+    """The packed query rows of one prefill call over a drawn workload."""
+    new_tokens: np.ndarray        # [B] int32 rows per sequence
+    query_start_loc: np.ndarray   # [B + 1] int32
+    query: torch.Tensor           # [T, Hq, D] q dtype (CPU)
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.new_tokens.max()) if len(self.new_tokens) else 0
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.query_start_loc[-1])
+
+
+def make_prefill_rows(wl: Workload, new_tokens, seed: Optional[int] = None) -> PrefillRows:
+    """Rows for a prefill call: n_b new tokens per sequence, by recipe
+    ("all",) (the whole sequence) | ("fixed", n) (clipped to L_b) |
+    ("list", [n_b ...]) (taken as given, may exceed L_b) | ("uniform", lo, hi)
+    (clipped to L_b); queries are normals rounded to the query dtype.  Drawn
+    from a generator of its own, so the workload's draws are unchanged."""
+    c = wl.cfg
+    rng = np.random.default_rng([c.seed if seed is None else seed, 0x70F1])
+    L = wl.seq_lens.astype(np.int64)
+    kind = new_tokens[0]
+    if kind == "all":
+        n = L.copy()
+    elif kind == "fixed":
+        n = np.minimum(L, int(new_tokens[1]))
+    elif kind == "list":
+        n = np.asarray(new_tokens[1], dtype=np.int64)
+        assert n.shape == L.shape
+    elif kind == "uniform":
+        n = np.minimum(L, rng.integers(int(new_tokens[1]), int(new_tokens[2]) + 1, size=len(L)))
+    else:
+        raise ValueError(f"unknown new-token recipe {new_tokens!r}")
+    qsl = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = _normals(rng, (int(qsl[-1]), c.num_q_heads, c.head_dim), c.q_dtype)
+    return PrefillRows(new_tokens=n.astype(np.int32), query_start_loc=qsl, query=q)
+
+
 def shrink(cfg: WorkloadConfig, **kw) -> WorkloadConfig:
     """A copy of a config with some fields replaced (for small test cases)."""
     return dataclasses.replace(cfg, **kw)
