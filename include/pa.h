@@ -173,7 +173,9 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
  *                                 query_start_loc[B] = T
  *   max_query_len   an upper bound of every n_b (sizes the grid; a smaller
  *                   value is still correct, only slower); <= 0 uses T
- *   scale, block_size (a multiple of 16), num_kv_heads: as for pa_decode
+ *   scale           score scale, positive and finite (1/sqrt(D) for standard
+ *                   attention)
+ *   block_size (a multiple of 16), num_kv_heads: as for pa_decode
  *   launch          stream (workspace and partitioning unused); NULL = null
  *                   stream
  * Supported head_dim: 128.  No workspace; deterministic.  Asynchronous on

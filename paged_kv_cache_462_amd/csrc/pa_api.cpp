@@ -399,7 +399,7 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
     return fail(PA_ERR_UNSUPPORTED, "rows, pool or table too large");
   if ((int64_t)block_tables->shape[1] * bs > (1LL << 30))
     return fail(PA_ERR_INVALID_ARG, "block table addresses too many tokens");
-  if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+  if (!isfinite(scale) || !(scale > 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
   const int64_t vec = 8;  // 16-bit elements per 16 bytes
   if (!aligned16(query->data) || query->stride[0] % vec || query->stride[1] % vec)
     return fail(PA_ERR_INVALID_ARG, "query rows must be 16-byte aligned");

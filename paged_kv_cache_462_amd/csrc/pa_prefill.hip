@@ -43,6 +43,8 @@
 //    P.V product, so that the weights keep ~16 significant bits (a single
 //    bf16 P uses most of the error budget of a 16-bit result).
 // Causal masking only touches the KV tiles that cross the wave's diagonal.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 #include "pa_prefill.h"
@@ -54,8 +56,17 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;                      // keys per KV tile
-constexpr int kQSub = 4;                     // 16-row query subtiles per wave
+#ifndef PA_PREFILL_QSUB
+#define PA_PREFILL_QSUB 2
+#endif
+#ifndef PA_PREFILL_WAVES_PER_EU
+#define PA_PREFILL_WAVES_PER_EU 2
+#endif
+constexpr int kQSub = PA_PREFILL_QSUB;       // 16-row query subtiles per wave
 constexpr int kBM = kWaves * kQSub * 16;     // query rows per workgroup
+// largest growth of a row max (log2 units) absorbed without rescaling the
+// accumulated output: weights stay below 2^8, far inside f16 / bf16 range
+constexpr float kLazyRescale = 8.0f;
 
 template <int KIND>
 struct Esz {
@@ -76,12 +87,15 @@ __device__ __forceinline__ i32x4 load_chunk(const char* p) {
 }
 
 template <int QK, int KVK, int D>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
+void prefill_mfma_kernel(PrefillParams p) {
   static_assert(D == 128, "one 16-byte chunk per lane of a 16-lane row");
   constexpr bool BF = QK == K_BF16;
   constexpr int C = D / 8;      // 16-bit chunks of 8 elements per row
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int ESZ = Esz<KVK>::v;
+  constexpr int kOne2 = BF ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
+  const i32x4 kOnes = i32x4{kOne2, kOne2, kOne2, kOne2};
   __shared__ i32x4 k_lds[2][kBN * C];
   __shared__ i32x4 v_lds[2][kBN * C];
 
@@ -105,6 +119,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
   // staging: thread -> row srow + 16 i of the KV tile, chunk sch
   const int srow = threadIdx.x >> 4;
   const int sch = threadIdx.x & 15;
+  // a 16-token subtile lies in one block: uniform base + this per-lane part
+  const uint32_t lane_off = (uint32_t)(srow * tok_bytes + sch * 8 * ESZ);
+  const int64_t blk_bytes = (int64_t)p.bs * tok_bytes;
 
   for (int tile = ntiles - 1 - rank; tile >= 0; tile -= p.tile_ranks) {
     const int row0 = tile * kBM;
@@ -127,33 +144,47 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
       for (int st = 0; st < KS; ++st) qf[qs][st] = *reinterpret_cast<const i32x4*>(qp + (4 * st + g) * 16);
     }
-    float m[kQSub], l[kQSub];
-    f32x4 o[kQSub][8];
+    // running max (log2 units), output and weight sum (every element of
+    // ls[qs] holds the sum of its lane's row)
+    float m[kQSub];
+    f32x4 o[kQSub][8], ls[kQSub];
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
       m[qs] = kMaxFloor;
-      l[qs] = 0.f;
+      ls[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[qs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // Block ids, 64 subtiles (16 KV tiles) per VGPR: lane i of chunk c
+    // holds the id of subtile 64c + i; the next chunk is fetched one chunk
+    // ahead, so reading an id (v_readlane) never waits on the table
+    auto fetch_ids = [&](int chunk) {
+      const int tok0 = (chunk * 64 + lane) * 16;
+      return tok0 < kv_end ? tab[tok0 / p.bs] : 0;
+    };
+    int ids_cur = fetch_ids(0), ids_nxt = fetch_ids(1), ids_chunk = 0;
+
     i32x4 kr[4], vr[4];
+    // raw chunks of the four 16-token subtiles of KV tile kt (nothing is
+    // done with them until they are stored, so no wait lands in the compute)
     auto load_tile = [&](int kt) {
+      if ((kt >> 4) != ids_chunk) {  // workgroup-uniform
+        ids_cur = ids_nxt;
+        ids_chunk = kt >> 4;
+        ids_nxt = fetch_ids(ids_chunk + 1);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int sub0 = kt * kBN + 16 * i;  // workgroup-uniform
-        kr[i] = i32x4{0, 0, 0, 0};
-        vr[i] = i32x4{0, 0, 0, 0};
-        if (sub0 < L) {
-          const int tok = sub0 + srow;
-          const int blk = tab[sub0 / p.bs];
-          const int64_t off = ((int64_t)blk * p.bs + tok % p.bs) * tok_bytes + sch * 8 * ESZ;
-          const i32x4 kx = load_chunk<KVK, BF>(kbase + off);
-          const i32x4 vx = load_chunk<KVK, BF>(vbase + off);
-          // slots past the sequence's end hold stale data: zero them
-          const bool live = tok < L;
-          kr[i] = live ? kx : i32x4{0, 0, 0, 0};
-          vr[i] = live ? vx : i32x4{0, 0, 0, 0};
+        if (sub0 < kv_end) {
+          const int blk = __builtin_amdgcn_readlane(ids_cur, (kt * 4 + i) & 63);
+          const int64_t ub = (int64_t)blk * blk_bytes + (int64_t)(sub0 % p.bs) * tok_bytes;
+          kr[i] = load_chunk<KVK, BF>(kbase + ub + lane_off);
+          vr[i] = load_chunk<KVK, BF>(vbase + ub + lane_off);
+        } else {
+          kr[i] = i32x4{0, 0, 0, 0};
+          vr[i] = i32x4{0, 0, 0, 0};
         }
       }
     };
@@ -162,18 +193,30 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
     if (ntk > 0) load_tile(0);
     for (int kt = 0; kt < ntk; ++kt) {
       const int buf = kt & 1;
+      const int key0 = kt * kBN;
+      if (key0 + kBN <= kv_end) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = srow + 16 * i;
-        k_lds[buf][r * C + (sch ^ srow)] = kr[i];
-        v_lds[buf][r * C + sch] = vr[i];
+        for (int i = 0; i < 4; ++i) {
+          const int r = srow + 16 * i;
+          k_lds[buf][r * C + (sch ^ srow)] = kr[i];
+          v_lds[buf][r * C + sch] = vr[i];
+        }
+      } else {
+        // the keys end inside this tile: slots past the sequence's end hold
+        // stale data, and keys past the tile's last row are never weighted
+        // (zero them so that 0 * stale never reaches the output)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = srow + 16 * i;
+          const bool live = key0 + r < kv_end;
+          k_lds[buf][r * C + (sch ^ srow)] = live ? kr[i] : i32x4{0, 0, 0, 0};
+          v_lds[buf][r * C + sch] = live ? vr[i] : i32x4{0, 0, 0, 0};
+        }
       }
       __syncthreads();
       if (kt + 1 < ntk) load_tile(kt + 1);
 
-      const int key0 = kt * kBN;
       if (key0 >= w_end) continue;  // every row of this wave is done
-      const bool need_mask = key0 + kBN - 1 > w_first;
 
       // scores^T for the 4 key subtiles x kQSub row subtiles
       f32x4 s[kQSub][4];
@@ -192,55 +235,68 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
         }
       }
 
-      // online softmax; P^T operands (keys 4g+e of subtiles 2s2 and 2s2+1)
+      // online softmax; P^T operands (keys 4g+e of subtiles 2s2 and 2s2+1).
+      // Only the KV tiles that cross the wave's diagonal take the mask.
       i32x4 ph[kQSub][2], pl[kQSub][2];
+      auto softmax = [&](auto masked) {
 #pragma unroll
-      for (int qs = 0; qs < kQSub; ++qs) {
-        float x[4][4];
-        float tmax = -INFINITY;
+        for (int qs = 0; qs < kQSub; ++qs) {
+          float x[4][4];
+          float tmax = -INFINITY;
+          const int lim = pos[qs] - key0 - 4 * g;  // keys ks*16+e <= lim are seen
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+          for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = s[qs][ks][e] * p.qk_scale_log2;
-            if (need_mask) v = key0 + ks * 16 + 4 * g + e <= pos[qs] ? v : -INFINITY;
-            x[ks][e] = v;
-            tmax = fmaxf(tmax, v);
+            for (int e = 0; e < 4; ++e) {
+              float v = s[qs][ks][e];
+              if constexpr (decltype(masked)::value) v = ks * 16 + e <= lim ? v : -INFINITY;
+              x[ks][e] = v;
+              tmax = fmaxf(tmax, v);
+            }
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+          // the scale is positive: the max of the scaled scores is the scaled
+          // max.  The reference max only moves when some row of the wave grew
+          // by more than kLazyRescale (log2 units): weights then stay below
+          // 2^kLazyRescale, and out and sum share the same reference, so the
+          // result is the same
+          const float mn = fmaxf(m[qs], tmax * p.qk_scale_log2);
+          if (__any(mn > m[qs] + kLazyRescale)) {
+            asm volatile("" ::);  // keep this a branch (rarely taken)
+            const float alpha = fast_exp2(m[qs] - mn);
+            m[qs] = mn;
+            ls[qs] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[qs][j] *= alpha;
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mn = fmaxf(m[qs], tmax);
-        const float alpha = fast_exp2(m[qs] - mn);
-        m[qs] = mn;
-        float sum = 0.f;
+          const float mref = m[qs];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+          for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[ks][e] = fast_exp2(x[ks][e] - mn);
-            sum += x[ks][e];
-          }
-        l[qs] = l[qs] * alpha + sum;
+            for (int e = 0; e < 4; ++e) x[ks][e] = fast_exp2(__builtin_fmaf(x[ks][e], p.qk_scale_log2, -mref));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[qs][j] *= alpha;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const float* a = x[2 * s2];
-          const float* c = x[2 * s2 + 1];
-          if constexpr (BF) {
-            const uint32_t h0 = pack_bf16(a[0], a[1]), h1 = pack_bf16(a[2], a[3]);
-            const uint32_t h2 = pack_bf16(c[0], c[1]), h3 = pack_bf16(c[2], c[3]);
-            ph[qs][s2] = i32x4{(int)h0, (int)h1, (int)h2, (int)h3};
-            pl[qs][s2] = i32x4{(int)pack_bf16(a[0] - bf16_lo(h0), a[1] - bf16_hi(h0)),
-                               (int)pack_bf16(a[2] - bf16_lo(h1), a[3] - bf16_hi(h1)),
-                               (int)pack_bf16(c[0] - bf16_lo(h2), c[1] - bf16_hi(h2)),
-                               (int)pack_bf16(c[2] - bf16_lo(h3), c[3] - bf16_hi(h3))};
-          } else {
-            ph[qs][s2] = i32x4{(int)pack_f16(a[0], a[1]), (int)pack_f16(a[2], a[3]),
-                               (int)pack_f16(c[0], c[1]), (int)pack_f16(c[2], c[3])};
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const float* a = x[2 * s2];
+            const float* c = x[2 * s2 + 1];
+            if constexpr (BF) {
+              const uint32_t h0 = pack_bf16(a[0], a[1]), h1 = pack_bf16(a[2], a[3]);
+              const uint32_t h2 = pack_bf16(c[0], c[1]), h3 = pack_bf16(c[2], c[3]);
+              ph[qs][s2] = i32x4{(int)h0, (int)h1, (int)h2, (int)h3};
+              pl[qs][s2] = i32x4{(int)pack_bf16(a[0] - bf16_lo(h0), a[1] - bf16_hi(h0)),
+                                 (int)pack_bf16(a[2] - bf16_lo(h1), a[3] - bf16_hi(h1)),
+                                 (int)pack_bf16(c[0] - bf16_lo(h2), c[1] - bf16_hi(h2)),
+                                 (int)pack_bf16(c[2] - bf16_lo(h3), c[3] - bf16_hi(h3))};
+            } else {
+              ph[qs][s2] = i32x4{(int)pack_f16(a[0], a[1]), (int)pack_f16(a[2], a[3]),
+                                 (int)pack_f16(c[0], c[1]), (int)pack_f16(c[2], c[3])};
+            }
           }
         }
-      }
+      };
+      if (key0 + kBN - 1 > w_first)
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
 
       // out^T += V^T . P^T, 32 keys per step
 #pragma unroll
@@ -265,15 +321,21 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillParams p)
             if constexpr (BF) o[qs][j] = mfma_k32<BF>(a, pl[qs][s2], o[qs][j]);
           }
         }
+        // the weight sums on the matrix cores too: a row of ones as V^T
+        // gives every lane its row's sum of exactly the weights the output
+        // took (cheaper than 32 adds and two cross-lane steps per tile)
+#pragma unroll
+        for (int qs = 0; qs < kQSub; ++qs) {
+          ls[qs] = mfma_k32<BF>(kOnes, ph[qs][s2], ls[qs]);
+          if constexpr (BF) ls[qs] = mfma_k32<BF>(kOnes, pl[qs][s2], ls[qs]);
+        }
       }
     }
 
     // normalise and store: lane holds dims 32g .. 32g+31 of its row
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
-      float lt = l[qs];
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      const float lt = ls[qs][0];
       const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
       const int row = wrow0 + qs * 16 + n16;
       if (row < n) {

@@ -242,6 +242,8 @@ def test_prefill_rejects_bad_group_and_scale():
     a = _prefill_args(Hq=6, Hkv=4)
     _expect(_call_prefill(a), _lib.PA_ERR_INVALID_ARG)
     _expect(_call_prefill(_prefill_args(), scale=float("inf")), _lib.PA_ERR_INVALID_ARG)
+    _expect(_call_prefill(_prefill_args(), scale=0.0), _lib.PA_ERR_INVALID_ARG)
+    _expect(_call_prefill(_prefill_args(), scale=-0.1), _lib.PA_ERR_INVALID_ARG)
 
 
 def test_prefill_empty_is_noop():
