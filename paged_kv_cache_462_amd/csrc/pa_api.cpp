@@ -434,6 +434,9 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   p.D = (int)D;
   p.bs = (int)bs;
   p.tile_ranks = (int)ranks;
+  p.spb_shift = -1;
+  for (int sh = 0; sh < 24; ++sh)
+    if ((int64_t)16 << sh == bs) p.spb_shift = sh;
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;

@@ -21,6 +21,7 @@ struct PrefillParams {
   int64_t tab_stride;     // block-table row stride
   int32_t B, Hq, Hkv, G, D, bs;
   int32_t tile_ranks;     // query-tile ranks in the grid (grid.y / B)
+  int32_t spb_shift;      // log2(bs / 16) when bs / 16 is a power of two, else -1
   float qk_scale_log2;    // scale * k_scale * log2(e)
   float v_scale;          // fp8 V scale (1 otherwise)
 };

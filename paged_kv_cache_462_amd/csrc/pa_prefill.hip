@@ -53,7 +53,10 @@ namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+constexpr int kWaves = PA_PREFILL_WAVES;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBN = 64;                      // keys per KV tile
 #ifndef PA_PREFILL_QSUB
@@ -64,6 +67,9 @@ constexpr int kBN = 64;                      // keys per KV tile
 #endif
 constexpr int kQSub = PA_PREFILL_QSUB;       // 16-row query subtiles per wave
 constexpr int kBM = kWaves * kQSub * 16;     // query rows per workgroup
+constexpr int kRowBytes = 128 * 2 + 16;      // LDS row: 128 16-bit values + pad
+constexpr int kStageRows = kThreads / 16;    // KV-tile rows one staging pass covers
+constexpr int kStagePasses = kBN / kStageRows;
 // largest growth of a row max (log2 units) absorbed without rescaling the
 // accumulated output: weights stay below 2^8, far inside f16 / bf16 range
 constexpr float kLazyRescale = 8.0f;
@@ -86,18 +92,29 @@ __device__ __forceinline__ i32x4 load_chunk(const char* p) {
   }
 }
 
+// LDS transpose read (ds_read_b64_tr_b16), 4 16-bit values
+__device__ __forceinline__ i32x2 lds_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) const char*)p);
+  return __builtin_bit_cast(i32x2, r);
+}
+
 template <int QK, int KVK, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillParams p) {
   static_assert(D == 128, "one 16-byte chunk per lane of a 16-lane row");
   constexpr bool BF = QK == K_BF16;
-  constexpr int C = D / 8;      // 16-bit chunks of 8 elements per row
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int ESZ = Esz<KVK>::v;
   constexpr int kOne2 = BF ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
   const i32x4 kOnes = i32x4{kOne2, kOne2, kOne2, kOne2};
-  __shared__ i32x4 k_lds[2][kBN * C];
-  __shared__ i32x4 v_lds[2][kBN * C];
+  // K and V tiles, double-buffered, rows padded to kRowBytes: 16
+  // consecutive rows start on 16 different 16-byte bank groups, so the
+  // operand reads below are conflict-free with plain (immediate-offset)
+  // addressing
+  __shared__ __attribute__((aligned(16))) char k_lds[2][kBN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char v_lds[2][kBN * kRowBytes];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -116,12 +133,18 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int64_t tok_bytes = (int64_t)p.Hkv * D * ESZ;
   const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
   const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
-  // staging: thread -> row srow + 16 i of the KV tile, chunk sch
+  // staging: thread -> row srow + kStageRows i of the KV tile, chunk sch;
+  // the 16-token subtile (srow >> 4) + (kStageRows / 16) i is wave-uniform
   const int srow = threadIdx.x >> 4;
   const int sch = threadIdx.x & 15;
   // a 16-token subtile lies in one block: uniform base + this per-lane part
-  const uint32_t lane_off = (uint32_t)(srow * tok_bytes + sch * 8 * ESZ);
+  const uint32_t lane_off = (uint32_t)((srow & 15) * tok_bytes + sch * 8 * ESZ);
   const int64_t blk_bytes = (int64_t)p.bs * tok_bytes;
+  // LDS byte offsets this lane reads from: the K operand (row n16 of a key
+  // subtile, chunk g of a k-step) and the V^T transpose source (row 4g +
+  // n16/4 of a 4-key group, dims 4 (n16 % 4) .. +3 of a 16-dim block)
+  const int k_rd = n16 * kRowBytes + g * 16;
+  const int v_rd = (4 * g + (n16 >> 2)) * kRowBytes + (n16 & 3) * 8;
 
   for (int tile = ntiles - 1 - rank; tile >= 0; tile -= p.tile_ranks) {
     const int row0 = tile * kBM;
@@ -165,7 +188,7 @@ void prefill_mfma_kernel(PrefillParams p) {
     };
     int ids_cur = fetch_ids(0), ids_nxt = fetch_ids(1), ids_chunk = 0;
 
-    i32x4 kr[4], vr[4];
+    i32x4 kr[kStagePasses], vr[kStagePasses];
     // raw chunks of the four 16-token subtiles of KV tile kt (nothing is
     // done with them until they are stored, so no wait lands in the compute)
     auto load_tile = [&](int kt) {
@@ -175,11 +198,13 @@ void prefill_mfma_kernel(PrefillParams p) {
         ids_nxt = fetch_ids(ids_chunk + 1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sub0 = kt * kBN + 16 * i;  // workgroup-uniform
+      for (int i = 0; i < kStagePasses; ++i) {
+        const int sub = kt * 4 + (srow >> 4) + (kStageRows / 16) * i;  // wave-uniform
+        const int sub0 = sub * 16;
         if (sub0 < kv_end) {
-          const int blk = __builtin_amdgcn_readlane(ids_cur, (kt * 4 + i) & 63);
-          const int64_t ub = (int64_t)blk * blk_bytes + (int64_t)(sub0 % p.bs) * tok_bytes;
+          const int blk = __builtin_amdgcn_readlane(ids_cur, sub & 63);
+          const int in_blk = p.spb_shift >= 0 ? (sub & ((1 << p.spb_shift) - 1)) * 16 : sub0 % p.bs;
+          const int64_t ub = (int64_t)blk * blk_bytes + (int64_t)in_blk * tok_bytes;
           kr[i] = load_chunk<KVK, BF>(kbase + ub + lane_off);
           vr[i] = load_chunk<KVK, BF>(vbase + ub + lane_off);
         } else {
@@ -196,21 +221,21 @@ void prefill_mfma_kernel(PrefillParams p) {
       const int key0 = kt * kBN;
       if (key0 + kBN <= kv_end) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = srow + 16 * i;
-          k_lds[buf][r * C + (sch ^ srow)] = kr[i];
-          v_lds[buf][r * C + sch] = vr[i];
+        for (int i = 0; i < kStagePasses; ++i) {
+          const int r = srow + kStageRows * i;
+          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowBytes + sch * 16]) = kr[i];
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowBytes + sch * 16]) = vr[i];
         }
       } else {
         // the keys end inside this tile: slots past the sequence's end hold
         // stale data, and keys past the tile's last row are never weighted
         // (zero them so that 0 * stale never reaches the output)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = srow + 16 * i;
+        for (int i = 0; i < kStagePasses; ++i) {
+          const int r = srow + kStageRows * i;
           const bool live = key0 + r < kv_end;
-          k_lds[buf][r * C + (sch ^ srow)] = live ? kr[i] : i32x4{0, 0, 0, 0};
-          v_lds[buf][r * C + sch] = live ? vr[i] : i32x4{0, 0, 0, 0};
+          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowBytes + sch * 16]) = live ? kr[i] : i32x4{0, 0, 0, 0};
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowBytes + sch * 16]) = live ? vr[i] : i32x4{0, 0, 0, 0};
         }
       }
       __syncthreads();
@@ -225,11 +250,10 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) s[qs][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int r = ks * 16 + n16;
+      for (int st = 0; st < KS; ++st) {
 #pragma unroll
-        for (int st = 0; st < KS; ++st) {
-          const i32x4 kf = k_lds[buf][r * C + ((4 * st + g) ^ n16)];
+        for (int ks = 0; ks < 4; ++ks) {
+          const i32x4 kf = *reinterpret_cast<const i32x4*>(&k_lds[buf][k_rd + ks * 16 * kRowBytes + st * 64]);
 #pragma unroll
           for (int qs = 0; qs < kQSub; ++qs) s[qs][ks] = mfma_k32<BF>(kf, qf[qs][st], s[qs][ks]);
         }
@@ -253,16 +277,18 @@ void prefill_mfma_kernel(PrefillParams p) {
               x[ks][e] = v;
               tmax = fmaxf(tmax, v);
             }
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-          // the scale is positive: the max of the scaled scores is the scaled
-          // max.  The reference max only moves when some row of the wave grew
-          // by more than kLazyRescale (log2 units): weights then stay below
-          // 2^kLazyRescale, and out and sum share the same reference, so the
-          // result is the same
-          const float mn = fmaxf(m[qs], tmax * p.qk_scale_log2);
-          if (__any(mn > m[qs] + kLazyRescale)) {
+          // The reference max m[qs] is shared by the four lanes of a row
+          // and only moves when some row of the wave has a score more than
+          // kLazyRescale (log2 units) above it; the per-tile check needs no
+          // cross-lane step (the scale is positive, so the scaled max is the
+          // max scaled).  Between moves the weights stay below
+          // 2^kLazyRescale, and output and sum share the reference, so the
+          // result is the same.
+          if (__any(tmax * p.qk_scale_log2 > m[qs] + kLazyRescale)) {
             asm volatile("" ::);  // keep this a branch (rarely taken)
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+            const float mn = fmaxf(m[qs], tmax * p.qk_scale_log2);
             const float alpha = fast_exp2(m[qs] - mn);
             m[qs] = mn;
             ls[qs] *= alpha;
@@ -298,27 +324,25 @@ void prefill_mfma_kernel(PrefillParams p) {
       else
         softmax(std::false_type{});
 
-      // out^T += V^T . P^T, 32 keys per step
+      // out^T += V^T . P^T, 32 keys per step.  The V^T operand of dims
+      // 16 jb .. 16 jb + 15 comes straight out of two LDS transpose reads
+      // (ds_read_b64_tr_b16): within each 16-lane group, lane j receives
+      // element j % 4 of the 8 bytes lane 4e + j / 4 points at, so with
+      // lane (g, j) pointing at row 4g + j/4 of a 4-key group, dims
+      // 16 jb + 4 (j % 4) .. +3, lane (g, j) gets dim 16 jb + j of keys
+      // 4g .. 4g+3 -- the k slots the score tile gave lane group g.
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        i32x4 vw[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = s2 * 32 + (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
-          vw[e] = v_lds[buf][key * C + n16];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int dw = j >> 1;
-          i32x4 a;
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr)
-            a[pr] = (int)((j & 1) ? pack_hi_halves((uint32_t)vw[2 * pr][dw], (uint32_t)vw[2 * pr + 1][dw])
-                                  : pack_lo_halves((uint32_t)vw[2 * pr][dw], (uint32_t)vw[2 * pr + 1][dw]));
+        for (int jb = 0; jb < 8; ++jb) {
+          const char* vp = &v_lds[buf][v_rd + s2 * 32 * kRowBytes + jb * 32];
+          const i32x2 lo = lds_tr16(vp);
+          const i32x2 hi = lds_tr16(vp + 16 * kRowBytes);
+          const i32x4 a = i32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qs = 0; qs < kQSub; ++qs) {
-            o[qs][j] = mfma_k32<BF>(a, ph[qs][s2], o[qs][j]);
-            if constexpr (BF) o[qs][j] = mfma_k32<BF>(a, pl[qs][s2], o[qs][j]);
+            o[qs][jb] = mfma_k32<BF>(a, ph[qs][s2], o[qs][jb]);
+            if constexpr (BF) o[qs][jb] = mfma_k32<BF>(a, pl[qs][s2], o[qs][jb]);
           }
         }
         // the weight sums on the matrix cores too: a row of ones as V^T
@@ -332,23 +356,20 @@ void prefill_mfma_kernel(PrefillParams p) {
       }
     }
 
-    // normalise and store: lane holds dims 32g .. 32g+31 of its row
+    // normalise and store: lane holds dims 16 jb + 4g .. 16 jb + 4g + 3
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
       const float lt = ls[qs][0];
       const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
       const int row = wrow0 + qs * 16 + n16;
       if (row < n) {
-        char* op = static_cast<char*>(p.out) + ((int64_t)(q0 + row) * p.o_st + (int64_t)h * p.o_sh + 32 * g) * 2;
+        char* op = static_cast<char*>(p.out) + ((int64_t)(q0 + row) * p.o_st + (int64_t)h * p.o_sh + 4 * g) * 2;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          i32x4 v;
-#pragma unroll
-          for (int pr = 0; pr < 4; ++pr) {
-            const float a0 = o[qs][2 * pr][i] * inv, a1 = o[qs][2 * pr + 1][i] * inv;
-            v[pr] = (int)(BF ? pack_bf16(a0, a1) : pack_f16(a0, a1));
-          }
-          *reinterpret_cast<i32x4*>(op + i * 16) = v;
+        for (int jb = 0; jb < 8; ++jb) {
+          const f32x4 v = o[qs][jb] * inv;
+          const i32x2 w2 = BF ? i32x2{(int)pack_bf16(v[0], v[1]), (int)pack_bf16(v[2], v[3])}
+                              : i32x2{(int)pack_f16(v[0], v[1]), (int)pack_f16(v[2], v[3])};
+          *reinterpret_cast<i32x2*>(op + jb * 32) = w2;
         }
       }
     }
