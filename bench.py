@@ -44,19 +44,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+DECODE_SOURCES = ("pa_decode.hip", "pa_device.h", "pa_internal.h")
+PREFILL_SOURCES = ("pa_prefill.hip", "pa_prefill.h", "pa_device.h", "pa_internal.h")
+
+
+def kernel_source_hash(files=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in ("pa_decode.hip", "pa_device.h", "pa_internal.h"):
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_462_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, launch_desc: str):
+def load_traffic(workload: str, launch_desc: str, kernel: str = "pa_decode",
+                 files=DECODE_SOURCES):
     """HBM bytes per launch from the committed counter summary
-    (profiles/pa_decode_<workload>_traffic.txt, `key: value` lines), if it was
-    taken on the current decode kernel source and launch plan."""
-    path = os.path.join(ROOT, "profiles", f"pa_decode_{workload}_traffic.txt")
+    (profiles/<kernel>_<workload>_traffic.txt, `key: value` lines), if it was
+    taken on the current kernel source and launch plan."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     t = {}
@@ -66,7 +71,7 @@ def load_traffic(workload: str, launch_desc: str):
                 continue
             k, v = line.split(":", 1)
             t[k.strip()] = v.strip()
-    if t.get("kernel_source_sha") != kernel_source_hash() or t.get("launch") != launch_desc:
+    if t.get("kernel_source_sha") != kernel_source_hash(files) or t.get("launch") != launch_desc:
         return None
     return {"hbm_bytes_per_launch": int(t["hbm_bytes_per_launch"])}
 
@@ -335,6 +340,11 @@ def bench_prefill(args) -> int:
     att_mean = float(np.mean(att_ms))
     flops = prefill_flops(rows, wl.seq_lens, c.num_q_heads, c.head_dim)
     achieved = flops / (att_mean * 1e-3) / 1e12
+    # algorithmic bytes: the query rows and outputs once, every sequence's
+    # cached K/V once
+    qo_bytes = 2 * rows.num_rows * c.num_q_heads * c.head_dim * q.element_size()
+    alg_bytes = qo_bytes + wl.logical_kv_bytes()
+    traffic = load_traffic(c.name, "default", "pa_prefill", PREFILL_SOURCES)
     res = {
         "metric": "paged causal prefill attention: TFLOP/s (algorithmic, unmasked part) and tokens/s",
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -371,8 +381,9 @@ def bench_prefill(args) -> int:
             "peak": MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": (traffic["hbm_bytes_per_launch"] if traffic else None),
             "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": alg_bytes,
             "mean_launch_ms": round(att_mean, 5),
             "median_launch_ms": round(float(np.median(att_ms)), 5),
         },

@@ -395,6 +395,7 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
     return fail(PA_ERR_INVALID_ARG, "block_tables column stride, seq_lens and query_start_loc strides must be 1");
   if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "batch above 65535");
   if (Hq > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 query heads");
+  if (Hq * B > (1LL << 24)) return fail(PA_ERR_UNSUPPORTED, "num_q_heads * batch above 2^24");
   if (T > 0x7FFFFFFFLL || N > 0x7FFFFFFFLL || block_tables->shape[1] > 0x7FFFFFFFLL)
     return fail(PA_ERR_UNSUPPORTED, "rows, pool or table too large");
   if ((int64_t)block_tables->shape[1] * bs > (1LL << 30))
@@ -412,7 +413,9 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   const int64_t bm = pa::prefill_rows_per_workgroup();
   const int64_t mq = max_query_len > 0 && max_query_len < T ? max_query_len : T;
   int64_t ranks = (mq + bm - 1) / bm;
-  if (ranks * B > 65535) ranks = 65535 / B;  // the kernel loops over the rest
+  // grid = Hq * ranks * B workgroups; past 2^24 the kernel loops instead
+  const int64_t per_rank = Hq * B;
+  if (ranks * per_rank > (1LL << 24)) ranks = (1LL << 24) / per_rank > 0 ? (1LL << 24) / per_rank : 1;
   pa::PrefillParams p;
   memset(&p, 0, sizeof p);
   p.out = out->data;
@@ -434,6 +437,7 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   p.D = (int)D;
   p.bs = (int)bs;
   p.tile_ranks = (int)ranks;
+  p.xcd_groups = (B * Hkv) % 8 == 0 ? (int)(B * Hkv / 8) : 0;
   p.spb_shift = -1;
   for (int sh = 0; sh < 24; ++sh)
     if ((int64_t)16 << sh == bs) p.spb_shift = sh;

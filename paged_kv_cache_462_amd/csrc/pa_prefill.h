@@ -20,8 +20,10 @@ struct PrefillParams {
   int64_t o_st, o_sh;     // output strides
   int64_t tab_stride;     // block-table row stride
   int32_t B, Hq, Hkv, G, D, bs;
-  int32_t tile_ranks;     // query-tile ranks in the grid (grid.y / B)
+  int32_t tile_ranks;     // query-tile ranks in the grid (grid.x / (Hq * B))
   int32_t spb_shift;      // log2(bs / 16) when bs / 16 is a power of two, else -1
+  int32_t xcd_groups;     // (sequence, kv head) groups per XCD when B * Hkv is a
+                          // multiple of 8, else 0 (plain order)
   float qk_scale_log2;    // scale * k_scale * log2(e)
   float v_scale;          // fp8 V scale (1 otherwise)
 };

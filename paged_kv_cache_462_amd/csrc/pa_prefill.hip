@@ -11,38 +11,44 @@
 // hundred query rows per tile this is a dense contraction, so both products
 // run on the matrix cores.
 //
-// Work decomposition.  A workgroup is four waves and takes one query head
-// and one tile of kBM consecutive rows of one sequence; each wave owns
-// kQSub 16-row subtiles.  The grid is (query head, tile rank x sequence):
-// rank 0 is the last (heaviest, it sees the most keys) tile of every
-// sequence, so the long tiles are dispatched first and the short ones fill
-// in at the end.  A workgroup walks the keys the tile needs, 64 at a time:
+// Work decomposition.  A workgroup is kWaves (8) waves and takes one query
+// head and one tile of kBM (256) consecutive rows of one sequence; each
+// wave owns kQSub (2) 16-row subtiles and two waves share a SIMD.  The grid
+// is (query head, tile rank x sequence): rank 0 is the last (heaviest, it
+// sees the most keys) tile of every sequence, so the long tiles are
+// dispatched first and the short ones fill in at the end; a grid with fewer
+// ranks than tiles loops.  A workgroup walks the keys its tile needs, 64 at
+// a time:
 //  * the four 16-token subtiles of a 64-key tile each lie inside one
-//    physical block (the block size is a multiple of 16), so their block
-//    ids are workgroup-uniform scalar loads from the table;
-//  * every thread loads four 16-byte chunks of K and of V rows (16 lanes
-//    per 256-byte row) into registers one tile ahead and writes them to a
-//    double-buffered LDS tile after the current tile's compute; K rows
-//    go in with an XOR swizzle of their 16-byte chunks so that the score
-//    operand reads (16 rows, one chunk) hit 16 different bank groups.
+//    physical block (the block size is a multiple of 16); the block ids of
+//    64 subtiles are prefetched into one VGPR, one chunk ahead, and read
+//    with v_readlane, so every K/V address is a scalar block base plus a
+//    per-lane offset and no table load sits between the K/V loads;
+//  * every thread loads 16-byte chunks of K and V rows (16 lanes per
+//    256-byte row) into registers one tile ahead and stores them to a
+//    double-buffered LDS tile at the top of the next iteration (slots past
+//    the keys the tile needs are zeroed there, so a stale NaN never meets a
+//    zero weight).  LDS rows are padded to 272 bytes: 16 consecutive rows
+//    start on 16 different 16-byte bank groups.
 // Per wave and KV tile:
 //  * scores^T[16 keys x 16 rows] = K[16 x D] . Q^T[D x 16] on
-//    v_mfma_f32_16x16x32; Q stays in registers for the whole tile.  Lane l
-//    gets keys 4*(l/16)+i of query row l%16;
+//    v_mfma_f32_16x16x32; Q stays in registers.  Lane l gets keys
+//    4*(l/16)+i of query row l%16;
 //  * online softmax per row in the exp2 domain (the score scale carries
-//    log2 e): the row max over the 64 keys needs two cross-lane steps (the
-//    four lanes l, l^16, l^32, l^48 share a row); the running sum stays
-//    per lane and is combined once at the end;
+//    log2 e).  The reference max is shared by the four lanes of a row and
+//    only moves (with a cross-lane max and a rescale of the output) when a
+//    score exceeds it by more than 2^8; otherwise the tile needs no
+//    cross-lane step at all.  The mask is applied only on the KV tiles that
+//    cross the wave's diagonal;
 //  * out^T[D x 16] += V^T[D x 32 keys] . P^T[32 keys x 16] on
 //    v_mfma_f32_16x16x32: the k index of that product runs over keys in
-//    the order the score tile left them in the lanes (keys 4g..4g+3 and
-//    16+4g..16+4g+3 for lane group g), so P^T needs no data movement; the
-//    V^T operand takes element j of 8 LDS rows (MFMA j, row m computes
-//    dim 8m + j), packed with v_perm;
+//    the order the score tile left them in the lanes, so P^T needs no data
+//    movement, and the V^T operand comes straight out of LDS transpose
+//    reads (ds_read_b64_tr_b16); a row of ones as V^T gives the weight sums
+//    on the matrix cores as well;
 //  * bf16 P is split into a high and a low bf16 part, each with its own
-//    P.V product, so that the weights keep ~16 significant bits (a single
-//    bf16 P uses most of the error budget of a 16-bit result).
-// Causal masking only touches the KV tiles that cross the wave's diagonal.
+//    product, so that the weights keep ~16 significant bits (a single bf16
+//    P uses most of the error budget of a 16-bit result).
 #include <type_traits>
 
 #include "pa_device.h"
@@ -120,9 +126,30 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
   const int g = lane >> 4;
-  const int h = blockIdx.x;
-  const int b = blockIdx.y % p.B;
-  const int rank = blockIdx.y / p.B;
+  // Workgroup id -> (query head, sequence, tile rank).  Workgroups are
+  // dealt to the eight XCDs round-robin (id % 8), each with its own L2.
+  // When the (sequence, kv head) groups split evenly over the XCDs, XCD x
+  // takes whole groups (every query head of the group, every tile), so a
+  // group's K/V is fetched into one L2 and reused there by all its query
+  // heads and tiles; inside an XCD the order is heaviest tile rank first.
+  int h, b, rank;
+  {
+    const int id = blockIdx.x;
+    if (p.xcd_groups) {
+      const int x = id & 7, slot = id >> 3;
+      const int per_rank = p.xcd_groups * p.G;  // items of one rank on an XCD
+      rank = slot / per_rank;
+      const int r2 = slot - rank * per_rank;
+      const int gi = (r2 / p.G) * 8 + x;        // (sequence, kv head) group
+      b = gi / p.Hkv;
+      h = (gi - b * p.Hkv) * p.G + r2 % p.G;
+    } else {
+      h = id % p.Hq;
+      const int y = id / p.Hq;
+      b = y % p.B;
+      rank = y / p.B;
+    }
+  }
   const int kvh = h / p.G;
   const int q0 = p.qsl[b];
   const int n = p.qsl[b + 1] - q0;
@@ -378,7 +405,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 
 template <int QK, int KVK, int D>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.Hq, (unsigned)(p.tile_ranks * p.B));
+  const dim3 grid((unsigned)(p.Hq * p.tile_ranks * p.B));
   hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

@@ -28,6 +28,11 @@ SMALL = {
     "fp8_bs32": (shrink(get_config("c5"), shared_prefix_tokens=0),
                  [777, 33, 96, 1],
                  ("list", [500, 33, 40, 1])),
+    # MQA (one kv head) with 3 sequences: batch x kv heads not a multiple of
+    # 8, so the workgroups take the plain (not XCD-grouped) order
+    "mqa_plain": (shrink(get_prefill_config("p1")[0], num_q_heads=8, num_kv_heads=1),
+                  [300, 40, 1],
+                  ("list", [300, 17, 1])),
     # fp16 query over an fp8 cache, group 4
     "fp8_f16q": (shrink(get_config("c5"), shared_prefix_tokens=0, q_dtype="f16", block_size=16),
                  [400, 260],
