@@ -1,7 +1,8 @@
 /*
- * pa.h -- C ABI of the MI355X (gfx950) paged decode-attention library.
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention library.
  *
- * The operation: single-query decode attention over a paged KV cache.  K and
+ * The operations: single-query decode attention (pa_decode) and causal
+ * multi-token prefill attention (pa_prefill) over a paged KV cache.  K and
  * V live in fixed-size physical blocks shaped
  * [num_blocks, block_size, num_kv_heads, head_dim]; each sequence reaches its
  * tokens through a row of a block table that maps logical block i (tokens
@@ -17,7 +18,9 @@
  *     lengths), question 9 (block allocator, reference counts), question 12
  *     (writing a new token at block = pos / bs, offset = pos % bs),
  *     question 13 (per-block loads inside the kernel), question 18
- *     (copy-on-write of a shared block), question 20 (shared prefix blocks);
+ *     (copy-on-write of a shared block), question 20 (shared prefix blocks),
+ *     question 6 (causal prefill), question 19 (query tiles against the
+ *     logical KV blocks with an online softmax);
  *   "KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践"
  *     (aiattnstudio.link), `PagedAttentionKernel.kernel_design` (kernel
  *     arguments: query, caches, block_tables, seq_lens, output, block size).

@@ -1,6 +1,6 @@
-"""CPU oracle for paged decode attention: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for paged decode and prefill attention: TEST INFRASTRUCTURE ONLY.
 
-A plain, slow, fp64 implementation of what the paged decode path computes,
+A plain, slow, fp64 implementation of what the paged attention path computes,
 written from the pages and checked against what they (and mathematics) fix.
 Only the test suite, the smoke check and the CPU-baseline leg of the
 benchmark may import it.  The product path (the C-ABI library, its kernels
@@ -22,6 +22,8 @@ Modules:
                  saturating quantiser
   sizing         KV-cache memory closed form and block-count arithmetic (O4)
   allocator      a Python model of the ref-counted LIFO block allocator (O4)
+  prefix_cache   a Python model of the prefix cache keyed by token prefixes
+  prefill        causal multi-token (prefill) attention over the cache (O5)
 
 Parity status: every function here is pinned by a test under tests/ that
 does not re-type its formula; see the module docstrings.
