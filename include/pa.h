@@ -181,7 +181,7 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
  *   block_size (a multiple of 16), num_kv_heads: as for pa_decode
  *   launch          stream (workspace and partitioning unused); NULL = null
  *                   stream
- * Supported head_dim: 128.  No workspace; deterministic.  Asynchronous on
+ * Supported head_dim: 64, 128.  No workspace; deterministic.  Asynchronous on
  * launch->stream.
  */
 int pa_prefill(pa_tensor* out, const pa_tensor* query,

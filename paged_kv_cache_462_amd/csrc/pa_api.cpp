@@ -151,7 +151,7 @@ const char* pa_last_error(void) { return g_err.c_str(); }
 const char* pa_build_info(void) {
   return "target gfx950 (CDNA4); decode VALU {f32,f16,bf16,fp8-kv} x head_dim {64,128} x "
          "heads/tile {1,2,4}; decode MFMA {f16,bf16,fp8-kv} x head_dim {64,128} x 16 heads/tile; "
-         "split-partition merge; prefill MFMA {f16,bf16} x {same,fp8} kv x head_dim 128; "
+         "split-partition merge; prefill MFMA {f16,bf16} x {same,fp8} kv x head_dim {64,128}; "
          "cache write {copy, fp8 e4m3 quantise}; block copy";
 }
 
@@ -407,7 +407,7 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   if (!aligned16(out->data) || out->stride[0] % vec || out->stride[1] % vec)
     return fail(PA_ERR_INVALID_ARG, "out rows must be 16-byte aligned");
   if (!pa::prefill_variant_built(kind_of(qdt), kind_of(kvdt), (int)D))
-    return fail(PA_ERR_UNSUPPORTED, "no prefill variant for this dtype / head_dim (head_dim 128 is built)");
+    return fail(PA_ERR_UNSUPPORTED, "no prefill variant for this dtype / head_dim (64 and 128 are built)");
   if (B == 0 || T == 0 || Hq == 0) return PA_OK;
 
   const int64_t bm = pa::prefill_rows_per_workgroup();

@@ -73,9 +73,6 @@ constexpr int kBN = 64;                      // keys per KV tile
 #endif
 constexpr int kQSub = PA_PREFILL_QSUB;       // 16-row query subtiles per wave
 constexpr int kBM = kWaves * kQSub * 16;     // query rows per workgroup
-constexpr int kRowBytes = 128 * 2 + 16;      // LDS row: 128 16-bit values + pad
-constexpr int kStageRows = kThreads / 16;    // KV-tile rows one staging pass covers
-constexpr int kStagePasses = kBN / kStageRows;
 // largest growth of a row max (log2 units) absorbed without rescaling the
 // accumulated output: weights stay below 2^8, far inside f16 / bf16 range
 constexpr float kLazyRescale = 8.0f;
@@ -109,8 +106,13 @@ __device__ __forceinline__ i32x2 lds_tr16(const char* p) {
 template <int QK, int KVK, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillParams p) {
-  static_assert(D == 128, "one 16-byte chunk per lane of a 16-lane row");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   constexpr bool BF = QK == K_BF16;
+  constexpr int CH = D / 8;                      // 16-byte chunks (8 values) per row
+  constexpr int DB = D / 16;                     // 16-dim output blocks
+  constexpr int kRowBytes = D * 2 + 16;          // LDS row: D 16-bit values + pad
+  constexpr int kStageRows = kThreads / CH;      // KV-tile rows one staging pass covers
+  constexpr int kStagePasses = kBN / kStageRows;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int ESZ = Esz<KVK>::v;
   constexpr int kOne2 = BF ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
@@ -161,9 +163,10 @@ void prefill_mfma_kernel(PrefillParams p) {
   const char* kbase = static_cast<const char*>(p.kc) + (int64_t)kvh * D * ESZ;
   const char* vbase = static_cast<const char*>(p.vc) + (int64_t)kvh * D * ESZ;
   // staging: thread -> row srow + kStageRows i of the KV tile, chunk sch;
-  // the 16-token subtile (srow >> 4) + (kStageRows / 16) i is wave-uniform
-  const int srow = threadIdx.x >> 4;
-  const int sch = threadIdx.x & 15;
+  // a wave covers 64 / CH consecutive rows of one 16-token subtile, so the
+  // subtile (srow >> 4) + (kStageRows / 16) i is wave-uniform
+  const int srow = threadIdx.x / CH;
+  const int sch = threadIdx.x % CH;
   // a 16-token subtile lies in one block: uniform base + this per-lane part
   const uint32_t lane_off = (uint32_t)((srow & 15) * tok_bytes + sch * 8 * ESZ);
   const int64_t blk_bytes = (int64_t)p.bs * tok_bytes;
@@ -197,13 +200,13 @@ void prefill_mfma_kernel(PrefillParams p) {
     // running max (log2 units), output and weight sum (every element of
     // ls[qs] holds the sum of its lane's row)
     float m[kQSub];
-    f32x4 o[kQSub][8], ls[kQSub];
+    f32x4 o[kQSub][DB], ls[kQSub];
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
       m[qs] = kMaxFloor;
       ls[qs] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) o[qs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < DB; ++j) o[qs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     // Block ids, 64 subtiles (16 KV tiles) per VGPR: lane i of chunk c
@@ -320,7 +323,7 @@ void prefill_mfma_kernel(PrefillParams p) {
             m[qs] = mn;
             ls[qs] *= alpha;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[qs][j] *= alpha;
+            for (int j = 0; j < DB; ++j) o[qs][j] *= alpha;
           }
           const float mref = m[qs];
 #pragma unroll
@@ -361,7 +364,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int jb = 0; jb < 8; ++jb) {
+        for (int jb = 0; jb < DB; ++jb) {
           const char* vp = &v_lds[buf][v_rd + s2 * 32 * kRowBytes + jb * 32];
           const i32x2 lo = lds_tr16(vp);
           const i32x2 hi = lds_tr16(vp + 16 * kRowBytes);
@@ -392,7 +395,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       if (row < n) {
         char* op = static_cast<char*>(p.out) + ((int64_t)(q0 + row) * p.o_st + (int64_t)h * p.o_sh + 4 * g) * 2;
 #pragma unroll
-        for (int jb = 0; jb < 8; ++jb) {
+        for (int jb = 0; jb < DB; ++jb) {
           const f32x4 v = o[qs][jb] * inv;
           const i32x2 w2 = BF ? i32x2{(int)pack_bf16(v[0], v[1]), (int)pack_bf16(v[2], v[3])}
                               : i32x2{(int)pack_f16(v[0], v[1]), (int)pack_f16(v[2], v[3])};
@@ -415,16 +418,20 @@ hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
 int prefill_rows_per_workgroup() { return kBM; }
 
 bool prefill_variant_built(int qkind, int kvkind, int D) {
-  if (D != 128) return false;
+  if (D != 64 && D != 128) return false;
   if (qkind != K_F16 && qkind != K_BF16) return false;
   return kvkind == qkind || kvkind == K_FP8;
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
   if (!prefill_variant_built(qkind, kvkind, p.D)) return hipErrorNotSupported;
-  if (qkind == K_F16)
-    return kvkind == K_FP8 ? launch_one<K_F16, K_FP8, 128>(p, stream) : launch_one<K_F16, K_F16, 128>(p, stream);
-  return kvkind == K_FP8 ? launch_one<K_BF16, K_FP8, 128>(p, stream) : launch_one<K_BF16, K_BF16, 128>(p, stream);
+  const bool fp8 = kvkind == K_FP8;
+  if (p.D == 64) {
+    if (qkind == K_F16) return fp8 ? launch_one<K_F16, K_FP8, 64>(p, stream) : launch_one<K_F16, K_F16, 64>(p, stream);
+    return fp8 ? launch_one<K_BF16, K_FP8, 64>(p, stream) : launch_one<K_BF16, K_BF16, 64>(p, stream);
+  }
+  if (qkind == K_F16) return fp8 ? launch_one<K_F16, K_FP8, 128>(p, stream) : launch_one<K_F16, K_F16, 128>(p, stream);
+  return fp8 ? launch_one<K_BF16, K_FP8, 128>(p, stream) : launch_one<K_BF16, K_BF16, 128>(p, stream);
 }
 
 }  // namespace pa

@@ -33,6 +33,17 @@ SMALL = {
     "mqa_plain": (shrink(get_prefill_config("p1")[0], num_q_heads=8, num_kv_heads=1),
                   [300, 40, 1],
                   ("list", [300, 17, 1])),
+    # head_dim 64: bf16 GQA, fp16 MHA with block size 32, fp8 K/V
+    "d64_bf16": (shrink(get_prefill_config("p2")[0], head_dim=64),
+                 [600, 130, 17],
+                 ("list", [600, 64, 20])),
+    "d64_f16_bs32": (shrink(get_prefill_config("p1")[0], head_dim=64, num_q_heads=8,
+                            num_kv_heads=8, block_size=32),
+                     [333, 64],
+                     ("list", [333, 1])),
+    "d64_fp8": (shrink(get_config("c5"), shared_prefix_tokens=0, head_dim=64),
+                [500, 77],
+                ("list", [260, 77])),
     # fp16 query over an fp8 cache, group 4
     "fp8_f16q": (shrink(get_config("c5"), shared_prefix_tokens=0, q_dtype="f16", block_size=16),
                  [400, 260],
