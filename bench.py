@@ -15,7 +15,9 @@ A back-to-back run on a single copy is reported beside it for context.
 Prints ONE JSON line:
   value           KV GB/s over the whole timed step (algorithmic KV bytes of
                   the batch / step time)
-  roofline        the decode call measured with HIP events on the launch
+  roofline        the decode call measured with HIP events (created without
+                  the system-scope fence, so recording them does not flush
+                  the caches between the timed launches) on the launch
                   stream: algorithmic KV bytes per launch / mean duration,
                   against the 8 TB/s HBM peak; `traffic` from the committed
                   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken
@@ -74,6 +76,54 @@ def load_traffic(workload: str, launch_desc: str, kernel: str = "pa_decode",
     if t.get("kernel_source_sha") != kernel_source_hash(files) or t.get("launch") != launch_desc:
         return None
     return {"hbm_bytes_per_launch": int(t["hbm_bytes_per_launch"])}
+
+
+class HipTimingEvents:
+    """HIP events for timing launches on a stream, created with
+    hipEventDisableSystemFence: recording one then skips the system-scope
+    fence (cache write-back and invalidate) that a default event performs,
+    which otherwise stalls and slows the work that follows it.  They are
+    used only for elapsed times, never to synchronise with the work."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(ev)
+        return ev
+
+    def record(self, ev, stream):
+        self._check(self.hip.hipEventRecord(ev, self.ct.c_void_p(stream.cuda_stream)), "hipEventRecord")
+
+    def elapsed_ms(self, a, b) -> float:
+        self._check(self.hip.hipEventSynchronize(b), "hipEventSynchronize")
+        ms = self.ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b), "hipEventElapsedTime")
+        return float(ms.value)
+
+    def close(self):
+        for ev in self.events:
+            self.hip.hipEventDestroy(ev)
+        self.events = []
 
 
 def cpu_baseline(wl, seconds: float):
@@ -325,18 +375,25 @@ def bench_prefill(args) -> int:
         step_attn()
     torch.cuda.synchronize()
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    log(f"[bench] timing {K} prefill steps")
+    timer = HipTimingEvents()
+    sampled = list(range(0, K, max(1, args.time_every)))
+    evs = {i: (timer.create(), timer.create()) for i in sampled}
+    log(f"[bench] timing {K} prefill steps ({len(sampled)} launches event-timed)")
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step_write()
-        evs[i][0].record(stream)
+        ev = evs.get(i)
+        if ev:
+            timer.record(ev[0], stream)
         step_attn()
-        evs[i][1].record(stream)
+        if ev:
+            timer.record(ev[1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
-    att_ms = [a.elapsed_time(b) for a, b in evs]
+    att_ms = [timer.elapsed_ms(a, b) for a, b in evs.values()]
+    timer.close()
     att_mean = float(np.mean(att_ms))
     flops = prefill_flops(rows, wl.seq_lens, c.num_q_heads, c.head_dim)
     achieved = flops / (att_mean * 1e-3) / 1e12
@@ -386,6 +443,7 @@ def bench_prefill(args) -> int:
             "algorithmic_bytes_per_launch": alg_bytes,
             "mean_launch_ms": round(att_mean, 5),
             "median_launch_ms": round(float(np.median(att_ms)), 5),
+            "event_timed_launches": len(att_ms),
         },
         "cpu_baseline": None,
     }
@@ -407,6 +465,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
     ap.add_argument("--hot-iters", type=int, default=20)
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="event-time the attention launch of every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "swap"],
@@ -493,31 +553,38 @@ def main() -> int:
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    log(f"[bench] timing {K} steps")
+    timer = HipTimingEvents()
+    # every time_every-th step brackets its decode call with timing events
+    # (each marker idles the GPU for a few microseconds)
+    sampled = list(range(0, K, max(1, args.time_every)))
+    evs = {i: (timer.create(), timer.create()) for i in sampled}
+    log(f"[bench] timing {K} steps ({len(sampled)} decode launches event-timed)")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         write(i % n_layers)
-        evs[i][0].record(stream)
+        ev = evs.get(i)
+        if ev:
+            timer.record(ev[0], stream)
         decode(i % n_layers)
-        evs[i][1].record(stream)
+        if ev:
+            timer.record(ev[1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_ms = [timer.elapsed_ms(a, b) for a, b in evs.values()]
     dec_mean = float(np.mean(dec_ms))
     dec_med = float(np.median(dec_ms))
 
     # context: the same copy decoded back to back (part of it stays in cache)
     hot_ms = []
     for _ in range(args.hot_iters):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+        a, b = timer.create(), timer.create()
+        timer.record(a, stream)
         decode(0)
-        b.record(stream)
-        b.synchronize()
-        hot_ms.append(a.elapsed_time(b))
+        timer.record(b, stream)
+        hot_ms.append(timer.elapsed_ms(a, b))
+    timer.close()
     hot_med = float(np.median(hot_ms)) if hot_ms else None
 
     kv_unique = wl.unique_kv_bytes()
@@ -537,6 +604,7 @@ def main() -> int:
         "algorithmic_bytes_per_launch": kv_unique,
         "mean_launch_ms": round(dec_mean, 5),
         "median_launch_ms": round(dec_med, 5),
+        "event_timed_launches": len(dec_ms),
         "kv_pool_copies": n_layers,
         "same_copy_back_to_back_median_ms": round(hot_med, 5) if hot_med else None,
         "same_copy_back_to_back_GBps": round(kv_unique / (hot_med * 1e-3) / 1e9, 1) if hot_med else None,
