@@ -465,6 +465,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
     ap.add_argument("--hot-iters", type=int, default=20)
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
     ap.add_argument("--time-every", type=int, default=4,
                     help="event-time the attention launch of every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -527,19 +529,36 @@ def main() -> int:
     new_v = wl.new_value().to(dev)
     new_slots = torch.from_numpy(wl.new_slots).to(dev)
     out = torch.empty_like(q)
-    ws_bytes = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
-                                         c.block_size, wl.max_blocks, args.partition_tokens)
+    shared = args.shared_prefix
+    if shared and not c.shared_prefix_tokens:
+        raise SystemExit(f"{c.name} has no shared prefix")
+    if shared:
+        ws_bytes = pa.decode_shared_prefix_workspace_bytes(
+            c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, wl.max_blocks,
+            c.shared_prefix_tokens)
+        prefix_blocks = torch.from_numpy(wl.shared_blocks.astype(np.int32)).to(dev)
+    else:
+        ws_bytes = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                             c.block_size, wl.max_blocks, args.partition_tokens)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     plan = pa.decode_plan(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                           c.block_size, wl.max_blocks, args.partition_tokens)
+    if shared:
+        plan["schedule"] = "balanced+shared-prefix"
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def decode(layer):
         k_, v_ = layers[layer]
-        pa.decode(out, q, k_, v_, tables, lens, wl.scale, c.block_size, c.num_kv_heads,
-                  k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, workspace=ws,
-                  partition_tokens=args.partition_tokens, path=args.path)
+        if shared:
+            pa.decode_shared_prefix(out, q, k_, v_, tables, lens, prefix_blocks,
+                                    c.shared_prefix_tokens, wl.scale, c.block_size,
+                                    c.num_kv_heads, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                                    kv_dtype=kvd, workspace=ws)
+        else:
+            pa.decode(out, q, k_, v_, tables, lens, wl.scale, c.block_size, c.num_kv_heads,
+                      k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, workspace=ws,
+                      partition_tokens=args.partition_tokens, path=args.path)
 
     def write(layer):
         k_, v_ = layers[layer]
@@ -595,7 +614,8 @@ def main() -> int:
     traffic = load_traffic(c.name, launch_desc)
     roof = {
         "bound": "hbm",
-        "kernel": "pa_decode" + (" (decode + merge kernels)" if plan["schedule"] != "single" else ""),
+        "kernel": ("pa_decode_shared_prefix (prefix pass + decode + merge kernels)" if shared else
+                   "pa_decode" + (" (decode + merge kernels)" if plan["schedule"] != "single" else "")),
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",

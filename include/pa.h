@@ -192,6 +192,46 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query,
                const pa_launch* launch);
 
 /*
+ * pa_decode_shared_prefix -- pa_decode for a batch whose sequences all start
+ * with the same cached prefix: the first prefix_tokens tokens of every
+ * sequence are the tokens of the blocks listed in prefix_blocks, shared
+ * through the block tables ("5.KV Cache 管理 & PagedAttention", question 20;
+ * "KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践",
+ * `HashBasedCaching`).  The result is pa_decode's.  The prefix part of the
+ * attention is taken once for the whole batch -- every query row of a kv
+ * head against the prefix keys, as one dense product on the matrix cores,
+ * each row limited to its sequence's length -- instead of once per
+ * sequence; the rest of every sequence goes through the decode kernels,
+ * and the merge kernel folds both partial results (the pages' rescale
+ * identity across pieces).
+ *   out, query, key_cache, value_cache, block_tables, seq_lens, scale,
+ *   block_size, num_kv_heads: as for pa_decode, with an f16 or bf16 query
+ *                 and a positive scale
+ *   prefix_blocks [>= prefix_tokens / block_size] i32 (device), contiguous
+ *   prefix_tokens a positive multiple of block_size; sequences shorter than
+ *                 it attend only their own length of it
+ *   launch        stream and workspace (16-byte aligned, at least
+ *                 pa_decode_shared_prefix_workspace_bytes); partition_tokens
+ *                 must be 0 (the plan is always the balanced schedule, so
+ *                 the batch is at most 2048 sequences)
+ * Supported head_dim: 64, 128.  Three launches (prefix pass, decode of the
+ * rest, merge), deterministic.
+ */
+int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query,
+                            const pa_tensor* key_cache, const pa_tensor* value_cache,
+                            const pa_tensor* block_tables, const pa_tensor* seq_lens,
+                            const pa_tensor* prefix_blocks, int32_t prefix_tokens,
+                            float scale, int32_t block_size, int32_t num_kv_heads,
+                            const pa_launch* launch);
+
+/* Workspace bytes pa_decode_shared_prefix needs; a negative status on
+ * invalid sizes. */
+int64_t pa_decode_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks,
+                                                int32_t prefix_tokens);
+
+/*
  * pa_copy_blocks -- device copy of whole physical blocks, the data step of
  * copy-on-write ("5.KV Cache 管理 & PagedAttention", question 18,
  * copy_block): for each row (src, dst) of block_pairs,

@@ -18,6 +18,8 @@ from .ops import (  # noqa: F401
     copy_blocks,
     decode,
     decode_plan,
+    decode_shared_prefix,
+    decode_shared_prefix_workspace_bytes,
     decode_workspace_bytes,
     prefill,
     reshape_and_cache,

@@ -59,6 +59,9 @@ SIGNATURES = {
     "pa_reshape_and_cache": (c_int32, [_T, _T, _T, _T, _T, _L]),
     "pa_decode": (c_int32, [_T, _T, _T, _T, _T, _T, c_float, c_int32, c_int32, _L]),
     "pa_prefill": (c_int32, [_T, _T, _T, _T, _T, _T, _T, c_int32, c_float, c_int32, c_int32, _L]),
+    "pa_decode_shared_prefix": (c_int32, [_T, _T, _T, _T, _T, _T, _T, c_int32, c_float, c_int32,
+                                          c_int32, _L]),
+    "pa_decode_shared_prefix_workspace_bytes": (c_int64, [c_int32] * 7),
     "pa_copy_blocks": (c_int32, [_T, _T, _T, _L]),
     "pa_swap_blocks": (c_int32, [_T, _T, _T, _T, _T, _L]),
     "pa_decode_workspace_bytes": (c_int64, [c_int32] * 7),

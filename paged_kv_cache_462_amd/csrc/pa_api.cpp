@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/pa.h"
@@ -142,48 +143,14 @@ int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Pl
   return PA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* pa_last_error(void) { return g_err.c_str(); }
-
-const char* pa_build_info(void) {
-  return "target gfx950 (CDNA4); decode VALU {f32,f16,bf16,fp8-kv} x head_dim {64,128} x "
-         "heads/tile {1,2,4}; decode MFMA {f16,bf16,fp8-kv} x head_dim {64,128} x 16 heads/tile; "
-         "split-partition merge; prefill MFMA {f16,bf16} x {same,fp8} kv x head_dim {64,128}; "
-         "cache write {copy, fp8 e4m3 quantise}; block copy";
-}
-
-int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                  int32_t head_dim, int32_t block_size, int32_t max_blocks,
-                                  int32_t partition_tokens) {
-  Plan p;
-  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
-                     partition_tokens, &p);
-  return rc ? rc : p.ws_bytes;
-}
-
-int pa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t block_size, int32_t max_blocks, int32_t partition_tokens,
-                   pa_decode_plan_info* info) {
-  if (!info) return fail(PA_ERR_INVALID_ARG, "null plan descriptor");
-  Plan p;
-  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
-                     partition_tokens, &p);
-  if (rc) return rc;
-  info->schedule = p.sched == pa::kSchedBalanced ? PA_SCHEDULE_BALANCED
-                   : p.split                     ? PA_SCHEDULE_PARTITIONS
-                                                 : PA_SCHEDULE_SINGLE;
-  info->partition_tokens = p.sched == pa::kSchedBalanced || !p.split ? 0 : p.part_tokens;
-  info->workspace_bytes = p.ws_bytes;
-  return PA_OK;
-}
-
-int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
-              const pa_tensor* value_cache, const pa_tensor* block_tables,
-              const pa_tensor* seq_lens, float scale, int32_t block_size,
-              int32_t num_kv_heads, const pa_launch* launch) {
+// Validation, plan and kernel parameters of a decode call (everything but
+// the launch); *empty is set when there is nothing to launch.
+int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+                 const pa_tensor* value_cache, const pa_tensor* block_tables,
+                 const pa_tensor* seq_lens, float scale, int32_t block_size,
+                 int32_t num_kv_heads, const pa_launch* launch, int64_t extra_ws_bytes,
+                 pa::DecodeParams* out_p, pa::DecodeVariant* out_v, Plan* out_plan, bool* empty) {
+  *empty = false;
   int rc;
   if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(out, "out", 3)) ||
       (rc = check_cache_pair(key_cache, value_cache)) ||
@@ -248,11 +215,15 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
   v.gt = v.path == 2 ? 16 : (G == 1 ? 1 : (G == 2 ? 2 : 4));
   if (!pa::decode_variant_built(v)) return fail(PA_ERR_UNSUPPORTED, "no decode variant for this dtype / head_dim");
   if (plan.split) {
-    if (!launch || !launch->workspace || launch->workspace_bytes < (size_t)plan.ws_bytes)
-      return fail(PA_ERR_WORKSPACE, "split decode needs %lld workspace bytes", (long long)plan.ws_bytes);
+    const int64_t need = plan.ws_bytes + extra_ws_bytes;
+    if (!launch || !launch->workspace || launch->workspace_bytes < (size_t)need)
+      return fail(PA_ERR_WORKSPACE, "split decode needs %lld workspace bytes", (long long)need);
     if (!aligned16(launch->workspace)) return fail(PA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   }
-  if (B == 0 || Hq == 0) return PA_OK;
+  if (B == 0 || Hq == 0) {
+    *empty = true;
+    return PA_OK;
+  }
 
   pa::DecodeParams p;
   memset(&p, 0, sizeof p);
@@ -297,8 +268,185 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
     p.ws_ml = p.ws_acc + plan.slots * Hq * D;
     p.ws_meta = reinterpret_cast<int32_t*>(p.ws_ml + plan.slots * Hq * 2);
   }
+  *out_p = p;
+  *out_v = v;
+  *out_plan = plan;
+  return PA_OK;
+}
+
+// How the shared-prefix pass splits its work: 256-row tiles of the batch's
+// (sequence, query head) rows per kv head, and the prefix keys in pieces of
+// a multiple of 64 keys, enough pieces to give the GPU
+// about 256 workgroups.
+struct PrefixPlan {
+  int pieces = 0, chunk = 0, row_tiles = 0;
+  int64_t extra_ws_bytes = 0;  // triples of the prefix pieces
+};
+
+PrefixPlan prefix_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int prefix_tokens) {
+  PrefixPlan pp;
+  const int64_t rows = B * (Hq / Hkv);
+  const int64_t bm = pa::prefill_rows_per_workgroup();
+  pp.row_tiles = (int)((rows + bm - 1) / bm);
+  const int64_t target = std::max<int64_t>(1, 256 / std::max<int64_t>(1, Hkv * pp.row_tiles));
+  const int64_t most = std::max<int64_t>(1, (prefix_tokens + 63) / 64);
+  const int64_t want = std::min(target, most);
+  pp.chunk = (int)(((prefix_tokens + want - 1) / want + 63) / 64 * 64);
+  pp.pieces = (prefix_tokens + pp.chunk - 1) / pp.chunk;
+  pp.extra_ws_bytes = B * pp.pieces * Hq * (D + 2) * (int64_t)sizeof(float);
+  return pp;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+const char* pa_build_info(void) {
+  return "target gfx950 (CDNA4); decode VALU {f32,f16,bf16,fp8-kv} x head_dim {64,128} x "
+         "heads/tile {1,2,4}; decode MFMA {f16,bf16,fp8-kv} x head_dim {64,128} x 16 heads/tile; "
+         "split-partition merge; prefill MFMA {f16,bf16} x {same,fp8} kv x head_dim {64,128}; "
+         "cache write {copy, fp8 e4m3 quantise}; block copy";
+}
+
+int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                                  int32_t partition_tokens) {
+  Plan p;
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
+                     partition_tokens, &p);
+  return rc ? rc : p.ws_bytes;
+}
+
+int pa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t block_size, int32_t max_blocks, int32_t partition_tokens,
+                   pa_decode_plan_info* info) {
+  if (!info) return fail(PA_ERR_INVALID_ARG, "null plan descriptor");
+  Plan p;
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks,
+                     partition_tokens, &p);
+  if (rc) return rc;
+  info->schedule = p.sched == pa::kSchedBalanced ? PA_SCHEDULE_BALANCED
+                   : p.split                     ? PA_SCHEDULE_PARTITIONS
+                                                 : PA_SCHEDULE_SINGLE;
+  info->partition_tokens = p.sched == pa::kSchedBalanced || !p.split ? 0 : p.part_tokens;
+  info->workspace_bytes = p.ws_bytes;
+  return PA_OK;
+}
+
+int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+              const pa_tensor* value_cache, const pa_tensor* block_tables,
+              const pa_tensor* seq_lens, float scale, int32_t block_size,
+              int32_t num_kv_heads, const pa_launch* launch) {
+  pa::DecodeParams p;
+  pa::DecodeVariant v;
+  Plan plan;
+  bool empty;
+  int rc = decode_setup(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
+                        block_size, num_kv_heads, launch, 0, &p, &v, &plan, &empty);
+  if (rc || empty) return rc;
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_decode(p, v, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int64_t pa_decode_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t block_size, int32_t max_blocks,
+                                                int32_t prefix_tokens) {
+  Plan p;
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, 0, &p);
+  if (rc) return rc;
+  if (p.sched != pa::kSchedBalanced)
+    return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode takes batches of at most %d",
+                pa::kBalancedMaxBatch);
+  if (prefix_tokens <= 0 || prefix_tokens % block_size)
+    return fail(PA_ERR_INVALID_ARG, "prefix_tokens must be a positive multiple of block_size");
+  return p.ws_bytes + prefix_plan(batch, num_q_heads, num_kv_heads, head_dim, prefix_tokens).extra_ws_bytes;
+}
+
+int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+                            const pa_tensor* value_cache, const pa_tensor* block_tables,
+                            const pa_tensor* seq_lens, const pa_tensor* prefix_blocks,
+                            int32_t prefix_tokens, float scale, int32_t block_size,
+                            int32_t num_kv_heads, const pa_launch* launch) {
+  int rc;
+  if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(prefix_blocks, "prefix_blocks", 1)))
+    return rc;
+  if (query->dtype != PA_F16 && query->dtype != PA_BF16)
+    return fail(PA_ERR_INVALID_ARG, "the shared-prefix decode needs an f16 or bf16 query");
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (block_size <= 0 || prefix_tokens <= 0 || prefix_tokens % block_size)
+    return fail(PA_ERR_INVALID_ARG, "prefix_tokens must be a positive multiple of block_size");
+  if (prefix_blocks->dtype != PA_I32 || prefix_blocks->shape[0] < prefix_tokens / block_size ||
+      (prefix_blocks->shape[0] > 1 && prefix_blocks->stride[0] != 1))
+    return fail(PA_ERR_INVALID_ARG, "prefix_blocks must be int32 [>= prefix_tokens / block_size], contiguous");
+  // the plan is always the balanced schedule (automatic partitioning)
+  pa_launch ln = launch ? *launch : pa_launch{nullptr, nullptr, 0, 0, 0};
+  if (ln.partition_tokens != 0)
+    return fail(PA_ERR_INVALID_ARG, "the shared-prefix decode plans its own pieces (partition_tokens 0)");
+  const int64_t B = query->shape[0], Hq = query->shape[1], D = query->shape[2];
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  const PrefixPlan pp = prefix_plan(B, Hq, num_kv_heads, D, prefix_tokens);
+  pa::DecodeParams p;
+  pa::DecodeVariant v;
+  Plan plan;
+  bool empty;
+  if ((rc = decode_setup(out, query, key_cache, value_cache, block_tables, seq_lens, scale, block_size,
+                         num_kv_heads, &ln, pp.extra_ws_bytes, &p, &v, &plan, &empty)))
+    return rc;
+  if (plan.sched != pa::kSchedBalanced)
+    return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode takes batches of at most %d",
+                pa::kBalancedMaxBatch);
+  if (!pa::prefill_variant_built(v.qkind, v.kvkind, (int)D))
+    return fail(PA_ERR_UNSUPPORTED, "no shared-prefix pass for this dtype / head_dim");
+  if ((int64_t)prefix_tokens > (int64_t)p.max_blocks * p.bs)
+    return fail(PA_ERR_INVALID_ARG, "prefix_tokens exceeds what the block table addresses");
+  if (empty) return PA_OK;
+  // workspace: acc [slots, Hq, D], (max, sum) [slots, Hq, 2], meta [B, 2],
+  // with the prefix pieces' slots after the decode's own
+  const int64_t slots = plan.slots + B * pp.pieces;
+  p.ws_acc = static_cast<float*>(ln.workspace);
+  p.ws_ml = p.ws_acc + slots * Hq * D;
+  p.ws_meta = reinterpret_cast<int32_t*>(p.ws_ml + slots * Hq * 2);
+  p.skip = prefix_tokens;
+  p.prefix_pieces = pp.pieces;
+  p.prefix_slot0 = (int32_t)plan.slots;
+
+  pa::PrefillParams f;
+  memset(&f, 0, sizeof f);
+  f.q = query->data;
+  f.kc = key_cache->data;
+  f.vc = value_cache->data;
+  f.tables = static_cast<const int32_t*>(prefix_blocks->data);
+  f.tab_stride = 0;
+  f.lens = p.lens;
+  f.q_st = query->stride[0];
+  f.q_sh = query->stride[1];
+  f.B = p.B;
+  f.Hq = p.Hq;
+  f.Hkv = p.Hkv;
+  f.G = p.G;
+  f.D = p.D;
+  f.bs = p.bs;
+  f.spb_shift = -1;
+  for (int sh = 0; sh < 24; ++sh)
+    if ((16 << sh) == p.bs) f.spb_shift = sh;
+  f.qk_scale_log2 = p.qk_scale_log2;
+  f.v_scale = p.v_scale;
+  f.ws_acc = p.ws_acc;
+  f.ws_ml = p.ws_ml;
+  f.pfx_slot0 = p.prefix_slot0;
+  f.pfx_pieces = pp.pieces;
+  f.pfx_tokens = prefix_tokens;
+  f.pfx_chunk = pp.chunk;
+  f.pfx_row_tiles = pp.row_tiles;
+  hipStream_t stream = static_cast<hipStream_t>(ln.stream);
+  hipError_t e = pa::launch_prefix_pass(f, v.qkind, v.kvkind, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefix pass launch failed: %s", hipGetErrorString(e));
+  e = pa::launch_decode(p, v, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return PA_OK;
 }

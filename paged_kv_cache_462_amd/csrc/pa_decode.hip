@@ -57,6 +57,8 @@
 // read with v_readlane, so every K/V address is a scalar 64-bit block base
 // plus a 32-bit per-lane offset; the next tile's loads are issued before the
 // current tile is computed.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -144,7 +146,7 @@ __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, i
   int carry = 0;
   for (int base = 0; base < p.B; base += blockDim.x) {
     const int b = base + threadIdx.x;
-    int x = b < p.B ? (clamp_len(p, b) + kTile - 1) / kTile : 0;
+    int x = b < p.B ? (max(clamp_len(p, b) - p.skip, 0) + kTile - 1) / kTile : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -216,12 +218,12 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
       Work wk;
       wk.b = b;
       wk.L = clamp_len(p, b);
-      wk.t_lo = a * kTile;
-      wk.t_hi = min(e * kTile, wk.L);
+      wk.t_lo = p.skip + a * kTile;
+      wk.t_hi = min(p.skip + e * kTile, wk.L);
       wk.n_tiles = e - a;
       // slots first + b .. first + b + pieces - 1 belong to sequence b:
       // first_wg(b) + b grows by at least pieces(b) from b to b + 1
-      f(wk, pieces > 1 ? first + b + (wi - first) : -1);
+      f(wk, pieces > 1 || p.prefix_pieces > 0 ? first + b + (wi - first) : -1);
     }
   } else {
     if (!has_unit) return;
@@ -858,53 +860,72 @@ __global__ __launch_bounds__(kMaxThreads) void decode_valu_kernel(const DecodePa
 
 // ============================================================================
 // Piece merge: out = sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) with
-// M = max_p m_p.  One 256-thread workgroup per (query head, sequence):
-// GROUPS groups of D/4 threads (4 dims each, 16-byte loads) each fold every
-// GROUPS-th piece into a running (max, sum, output), loads of up to four
-// pieces in flight at once; then the group states are combined in group
-// order (a fixed order: the result does not depend on timing).  The piece
-// plan comes from the decode kernel (balanced schedule: per-sequence first
-// slot and piece count, 0 pieces for an empty sequence, whose zero row is
-// written here) or from the partition size (fixed schedule).
+// M = max_p m_p.  A 256-thread workgroup takes R (query head, sequence)
+// rows, consecutive heads of one sequence; each row gets GROUPS groups of
+// D/4 threads (4 dims each, 16-byte loads) that fold every GROUPS-th piece
+// into a running (max, sum, output), loads of up to four pieces in flight at
+// once; then a row's group states are combined in group order (a fixed
+// order: the result does not depend on timing).  Plans with many pieces per
+// row take R = 1 (eight groups folding side by side), plans with few take
+// more rows per workgroup, so that the launch is not thousands of
+// workgroups that each wait on one dependent load.  The piece plan comes
+// from the decode kernel (balanced schedule: per-sequence first slot and
+// piece count, 0 pieces for an empty sequence, whose zero row is written
+// here) or from the partition size (fixed schedule).
 // ============================================================================
 constexpr int kMergeThreads = 256;
 
-template <int QK, int D>
+template <int QK, int D, int R>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams p) {
-  constexpr int TPR = D / 4;                   // threads per piece row
-  constexpr int GROUPS = kMergeThreads / TPR;  // pieces folded side by side
-  constexpr int U = 4;                         // pieces in flight per group
-  __shared__ f32x4 s_num[GROUPS][TPR];
-  __shared__ float s_m[GROUPS], s_den[GROUPS];
+  constexpr int TPR = D / 4;                        // threads per piece row
+  constexpr int GROUPS = kMergeThreads / (TPR * R);  // pieces folded side by side per row
+  constexpr int U = 4;                              // pieces in flight per group
+  static_assert(GROUPS >= 1, "rows per workgroup");
+  __shared__ f32x4 s_num[R][GROUPS][TPR];
+  __shared__ float s_m[R][GROUPS], s_den[R][GROUPS];
 
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
   const int tid = threadIdx.x;
+  const int rr = tid / (GROUPS * TPR);  // row of the workgroup
+  const int t2 = tid - rr * GROUPS * TPR;
+  const int grp = t2 / TPR;
+  const int c = t2 - grp * TPR;
+  const int row = blockIdx.x * R + rr;
+  const bool live = row < p.B * p.Hq;
+  const int b = live ? row / p.Hq : 0;
+  const int h = live ? row - b * p.Hq : 0;
   const int64_t ob = (int64_t)b * p.o_sb + (int64_t)h * p.o_sh;
-  int slot0, P;
-  if (p.sched == kSchedBalanced) {
-    slot0 = p.ws_meta[2 * b];
-    P = p.ws_meta[2 * b + 1];
-    if (P == 0) {
-      if (tid < TPR) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        store_out_vec<QK, 4>(p.out, ob + 4 * tid, z);
+  int slot0 = 0, PS = 0, P = 0;  // PS pieces of this pass at slots slot0 .., P in all
+  bool direct = !live;           // nothing to merge for this row
+  if (live) {
+    if (p.sched == kSchedBalanced) {
+      slot0 = p.ws_meta[2 * b];
+      PS = p.ws_meta[2 * b + 1];
+      P = PS + p.prefix_pieces;
+      if (P == 0) {
+        if (grp == 0) {
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          store_out_vec<QK, 4>(p.out, ob + 4 * c, z);
+        }
+        direct = true;
       }
-      return;
+      if (P == 1 && p.prefix_pieces == 0) direct = true;  // single piece: written directly
+    } else {
+      const int L = clamp_len(p, b);
+      if (L <= p.part_tokens) {
+        direct = true;  // single partition: written directly
+      } else {
+        slot0 = b * p.num_parts;
+        P = PS = (L + p.part_tokens - 1) / p.part_tokens;
+      }
     }
-    if (P == 1) return;  // single piece: written directly
-  } else {
-    const int L = clamp_len(p, b);
-    if (L <= p.part_tokens) return;  // single partition: written directly
-    slot0 = b * p.num_parts;
-    P = (L + p.part_tokens - 1) / p.part_tokens;
   }
-  // triple of piece q: index base + q * Hq
-  const int64_t base = triple_index(p, slot0, h);
-  const int64_t step = p.Hq;
+  if (direct) P = 0;
+  // triple index of piece q: this pass's pieces, then the prefix pass's
+  auto piece_index = [&](int q) -> int64_t {
+    const int slot = q < PS ? slot0 + q : p.prefix_slot0 + b * p.prefix_pieces + (q - PS);
+    return triple_index(p, slot, h);
+  };
 
-  const int grp = tid / TPR;
-  const int c = tid - grp * TPR;
   float M = kMaxFloor, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = grp; q0 < P; q0 += U * GROUPS) {
@@ -915,7 +936,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int q = min(q0 + u * GROUPS, P - 1);
-      const int64_t ti = base + q * step;
+      const int64_t ti = piece_index(q);
       mq[u] = p.ws_ml[2 * ti];
       lq[u] = p.ws_ml[2 * ti + 1];
       aq[u] = *reinterpret_cast<const f32x4*>(p.ws_acc + ti * D + 4 * c);
@@ -937,33 +958,55 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams
       M = mn;
     }
   }
-  s_num[grp][c] = num;
-  if (c == 0) {
-    s_m[grp] = M;
-    s_den[grp] = den;
-  }
-  __syncthreads();
-  if (tid >= TPR) return;
-  float Mt = s_m[0];
+  if constexpr (GROUPS == 1) {
+    if (direct) return;
+    const float sc = den > 0.f ? p.v_scale / den : 0.f;
+    const float x[4] = {num[0] * sc, num[1] * sc, num[2] * sc, num[3] * sc};
+    store_out_vec<QK, 4>(p.out, ob + 4 * c, x);
+  } else {
+    s_num[rr][grp][c] = num;
+    if (c == 0) {
+      s_m[rr][grp] = M;
+      s_den[rr][grp] = den;
+    }
+    __syncthreads();
+    if (direct || grp != 0) return;
+    float Mt = s_m[rr][0];
 #pragma unroll
-  for (int k = 1; k < GROUPS; ++k) Mt = fmaxf(Mt, s_m[k]);
-  f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-  float dtot = 0.f;
+    for (int k = 1; k < GROUPS; ++k) Mt = fmaxf(Mt, s_m[rr][k]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float dtot = 0.f;
 #pragma unroll
-  for (int k = 0; k < GROUPS; ++k) {
-    const float sc = fast_exp2(s_m[k] - Mt);
-    tot += s_num[k][tid] * sc;
-    dtot += s_den[k] * sc;
+    for (int k = 0; k < GROUPS; ++k) {
+      const float sc = fast_exp2(s_m[rr][k] - Mt);
+      tot += s_num[rr][k][c] * sc;
+      dtot += s_den[rr][k] * sc;
+    }
+    const float sc = dtot > 0.f ? p.v_scale / dtot : 0.f;
+    const float x[4] = {tot[0] * sc, tot[1] * sc, tot[2] * sc, tot[3] * sc};
+    store_out_vec<QK, 4>(p.out, ob + 4 * c, x);
   }
-  const float sc = dtot > 0.f ? p.v_scale / dtot : 0.f;
-  const float x[4] = {tot[0] * sc, tot[1] * sc, tot[2] * sc, tot[3] * sc};
-  store_out_vec<QK, 4>(p.out, ob + 4 * tid, x);
 }
 
+// Rows per merge workgroup from the expected pieces per row: the balanced
+// plan deals 256 shares over the batch (about 256 / B + 1 pieces per
+// sequence, plus the prefix pass's), the fixed plan splits long sequences
+// into num_parts.
 template <int QK, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((merge_kernel<QK, D>), dim3(p.Hq, p.B), dim3(kMergeThreads), 0, stream, p);
-  return hipGetLastError();
+  const int pieces = p.sched == kSchedBalanced
+                         ? kBalancedWorkgroups / max(p.B, 1) + 1 + p.prefix_pieces
+                         : p.num_parts;
+  const int rows = p.B * p.Hq;
+  auto go = [&](auto rtag) {
+    constexpr int R = decltype(rtag)::value;
+    hipLaunchKernelGGL((merge_kernel<QK, D, R>), dim3((rows + R - 1) / R), dim3(kMergeThreads), 0, stream, p);
+    return hipGetLastError();
+  };
+  if (pieces > 16) return go(std::integral_constant<int, 1>{});
+  if (pieces > 8) return go(std::integral_constant<int, 2>{});
+  if (pieces > 4) return go(std::integral_constant<int, 4>{});
+  return go(std::integral_constant<int, 8>{});
 }
 
 template <int QK, int KVK, int D>

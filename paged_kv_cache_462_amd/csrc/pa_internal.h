@@ -48,6 +48,14 @@ struct DecodeParams {
   int32_t split;          // 1: pieces may leave triples, merged afterwards
   float qk_scale_log2;    // scale * k_scale * log2(e)
   float v_scale;          // fp8 V scale (1 otherwise)
+  // Shared-prefix split (balanced schedule only): the first `skip` tokens
+  // of every sequence are attended by a separate pass that leaves
+  // `prefix_pieces` triples per (sequence, query head) at slots
+  // prefix_slot0 + b * prefix_pieces + k; this pass covers the rest and
+  // every one of its pieces leaves a triple.  All 0 for plain decode.
+  int32_t skip;
+  int32_t prefix_pieces;
+  int32_t prefix_slot0;
 };
 
 struct DecodeVariant {

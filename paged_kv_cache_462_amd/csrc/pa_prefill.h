@@ -26,6 +26,16 @@ struct PrefillParams {
                           // multiple of 8, else 0 (plain order)
   float qk_scale_log2;    // scale * k_scale * log2(e)
   float v_scale;          // fp8 V scale (1 otherwise)
+  // Shared-prefix pass of a decode batch (prefix_pass_* launch): the rows
+  // are every (sequence, query head) of one kv head, the keys the first
+  // pfx_tokens tokens (blocks listed in `tables`, tab_stride 0), row b's
+  // limited to min(lens[b], pfx_tokens); q_st is the query's sequence
+  // stride.  Workgroup (kv head, row tile, key piece) leaves one (max, sum,
+  // unnormalised output) triple per row at slot pfx_slot0 + b * pfx_pieces
+  // + piece of ws_acc [slots, Hq, D] / ws_ml [slots, Hq, 2].
+  float* ws_acc;
+  float* ws_ml;
+  int32_t pfx_slot0, pfx_pieces, pfx_tokens, pfx_chunk, pfx_row_tiles;
 };
 
 // Query rows one workgroup takes.
@@ -35,5 +45,9 @@ int prefill_rows_per_workgroup();
 hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream);
 
 bool prefill_variant_built(int qkind, int kvkind, int D);
+
+// The shared-prefix pass (same variants as prefill); grid Hkv * pfx_row_tiles
+// * pfx_pieces workgroups.
+hipError_t launch_prefix_pass(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream);
 
 }  // namespace pa

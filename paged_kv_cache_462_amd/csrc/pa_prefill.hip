@@ -103,7 +103,11 @@ __device__ __forceinline__ i32x2 lds_tr16(const char* p) {
   return __builtin_bit_cast(i32x2, r);
 }
 
-template <int QK, int KVK, int D>
+// PFX = false: causal prefill.  PFX = true: the shared-prefix pass of a
+// decode batch (see PrefillParams): the same tile machinery with rows taken
+// from every sequence, a per-row key limit instead of the causal one, one
+// key piece per workgroup, and triples instead of normalised rows.
+template <int QK, int KVK, int D, bool PFX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
@@ -134,8 +138,17 @@ void prefill_mfma_kernel(PrefillParams p) {
   // takes whole groups (every query head of the group, every tile), so a
   // group's K/V is fetched into one L2 and reused there by all its query
   // heads and tiles; inside an XCD the order is heaviest tile rank first.
-  int h, b, rank;
-  {
+  int h, b, rank, kvh, piece = 0;
+  if constexpr (PFX) {
+    // (kv head, key piece, row tile), row tiles fastest
+    const int id = blockIdx.x;
+    rank = id % p.pfx_row_tiles;
+    const int t2 = id / p.pfx_row_tiles;
+    piece = t2 % p.pfx_pieces;
+    kvh = t2 / p.pfx_pieces;
+    h = kvh * p.G;
+    b = 0;
+  } else {
     const int id = blockIdx.x;
     if (p.xcd_groups) {
       const int x = id & 7, slot = id >> 3;
@@ -151,11 +164,12 @@ void prefill_mfma_kernel(PrefillParams p) {
       b = y % p.B;
       rank = y / p.B;
     }
+    kvh = h / p.G;
   }
-  const int kvh = h / p.G;
-  const int q0 = p.qsl[b];
-  const int n = p.qsl[b + 1] - q0;
-  const int L = p.lens[b];
+  // causal: rows of sequence b; prefix pass: all B * G (sequence, head) rows
+  const int q0 = PFX ? 0 : p.qsl[b];
+  const int n = PFX ? p.B * p.G : p.qsl[b + 1] - q0;
+  const int L = PFX ? p.pfx_tokens : p.lens[b];
   const int ntiles = (n + kBM - 1) / kBM;
   const int ctx = L - n;  // position of row 0 (negative when n > L)
   const int32_t* tab = p.tables + (int64_t)b * p.tab_stride;
@@ -176,26 +190,58 @@ void prefill_mfma_kernel(PrefillParams p) {
   const int k_rd = n16 * kRowBytes + g * 16;
   const int v_rd = (4 * g + (n16 >> 2)) * kRowBytes + (n16 & 3) * 8;
 
-  for (int tile = ntiles - 1 - rank; tile >= 0; tile -= p.tile_ranks) {
+  // causal: heaviest tile first, looping when the grid has fewer ranks than
+  // tiles; prefix pass: exactly row tile `rank`
+  for (int tile = PFX ? rank : ntiles - 1 - rank; tile >= 0; tile = PFX ? -1 : tile - p.tile_ranks) {
     const int row0 = tile * kBM;
     const int rows = min(kBM, n - row0);
-    const int kv_end = min(L, ctx + row0 + rows);  // keys [0, kv_end)
+    // keys [k_begin, kv_end) of this workgroup
+    const int k_begin = PFX ? piece * p.pfx_chunk : 0;
+    const int kv_end = PFX ? min(L, k_begin + p.pfx_chunk) : min(L, ctx + row0 + rows);
+    const int kt0 = k_begin / kBN;
     const int ntk = kv_end > 0 ? (kv_end + kBN - 1) / kBN : 0;
     const int wrow0 = row0 + w * kQSub * 16;
     const int wrows = max(0, min(kQSub * 16, n - wrow0));
-    const int w_end = wrows > 0 ? min(L, ctx + wrow0 + wrows) : 0;
-    const int w_first = ctx + wrow0;
 
     i32x4 qf[kQSub][KS];
-    int pos[kQSub];
+    int pos[kQSub];  // the row sees keys 0 .. pos
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
       const int row = wrow0 + qs * 16 + n16;
       const int rc = min(row, n - 1);
-      pos[qs] = ctx + row;
-      const char* qp = static_cast<const char*>(p.q) + ((int64_t)(q0 + rc) * p.q_st + (int64_t)h * p.q_sh) * 2;
+      int64_t qoff;
+      if constexpr (PFX) {
+        // row = b * G + j: sequence b, query head kvh * G + j
+        const int rb = rc / p.G;
+        pos[qs] = row < n ? min(max(p.lens[rb], 0), L) - 1 : -1;
+        qoff = (int64_t)rb * p.q_st + (int64_t)(h + rc - rb * p.G) * p.q_sh;
+      } else {
+        pos[qs] = ctx + row;
+        qoff = (int64_t)(q0 + rc) * p.q_st + (int64_t)h * p.q_sh;
+      }
+      const char* qp = static_cast<const char*>(p.q) + qoff * 2;
 #pragma unroll
       for (int st = 0; st < KS; ++st) qf[qs][st] = *reinterpret_cast<const i32x4*>(qp + (4 * st + g) * 16);
+    }
+    // keys this wave needs: [.., w_end); the mask is needed from w_first on
+    int w_end, w_first;
+    if constexpr (PFX) {
+      int hi = -1, lo = 1 << 30;
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs) {
+        hi = max(hi, pos[qs]);
+        lo = min(lo, pos[qs]);
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        hi = max(hi, __shfl_xor(hi, off));
+        lo = min(lo, __shfl_xor(lo, off));
+      }
+      w_end = min(kv_end, hi + 1);
+      w_first = lo;
+    } else {
+      w_end = wrows > 0 ? min(L, ctx + wrow0 + wrows) : 0;
+      w_first = ctx + wrow0;
     }
     // running max (log2 units), output and weight sum (every element of
     // ls[qs] holds the sum of its lane's row)
@@ -216,7 +262,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       const int tok0 = (chunk * 64 + lane) * 16;
       return tok0 < kv_end ? tab[tok0 / p.bs] : 0;
     };
-    int ids_cur = fetch_ids(0), ids_nxt = fetch_ids(1), ids_chunk = 0;
+    int ids_cur = fetch_ids(kt0 >> 4), ids_nxt = fetch_ids((kt0 >> 4) + 1), ids_chunk = kt0 >> 4;
 
     i32x4 kr[kStagePasses], vr[kStagePasses];
     // raw chunks of the four 16-token subtiles of KV tile kt (nothing is
@@ -245,8 +291,8 @@ void prefill_mfma_kernel(PrefillParams p) {
     };
 
     __syncthreads();  // the previous tile's last KV tile is no longer read
-    if (ntk > 0) load_tile(0);
-    for (int kt = 0; kt < ntk; ++kt) {
+    if (ntk > kt0) load_tile(kt0);
+    for (int kt = kt0; kt < ntk; ++kt) {
       const int buf = kt & 1;
       const int key0 = kt * kBN;
       if (key0 + kBN <= kv_end) {
@@ -386,6 +432,26 @@ void prefill_mfma_kernel(PrefillParams p) {
       }
     }
 
+    if constexpr (PFX) {
+      // this piece's triple of every row: (max, sum) and the unnormalised
+      // output, lane holding dims 16 jb + 4g .. +3
+#pragma unroll
+      for (int qs = 0; qs < kQSub; ++qs) {
+        const int row = wrow0 + qs * 16 + n16;
+        if (row < n) {
+          const int rb = row / p.G;
+          const int64_t ti = (int64_t)(p.pfx_slot0 + rb * p.pfx_pieces + piece) * p.Hq + h + (row - rb * p.G);
+          float* acc = p.ws_acc + ti * D + 4 * g;
+#pragma unroll
+          for (int jb = 0; jb < DB; ++jb) *reinterpret_cast<f32x4*>(acc + jb * 16) = o[qs][jb];
+          if (g == 0) {
+            p.ws_ml[2 * ti] = m[qs];
+            p.ws_ml[2 * ti + 1] = ls[qs][0];
+          }
+        }
+      }
+      continue;
+    }
     // normalise and store: lane holds dims 16 jb + 4g .. 16 jb + 4g + 3
 #pragma unroll
     for (int qs = 0; qs < kQSub; ++qs) {
@@ -406,11 +472,26 @@ void prefill_mfma_kernel(PrefillParams p) {
   }
 }
 
-template <int QK, int KVK, int D>
+template <int QK, int KVK, int D, bool PFX>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.Hq * p.tile_ranks * p.B));
-  hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D>), grid, dim3(kThreads), 0, stream, p);
+  const dim3 grid(PFX ? (unsigned)(p.Hkv * p.pfx_row_tiles * p.pfx_pieces)
+                      : (unsigned)(p.Hq * p.tile_ranks * p.B));
+  hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D, PFX>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool PFX>
+hipError_t launch_mode(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
+  if (!prefill_variant_built(qkind, kvkind, p.D)) return hipErrorNotSupported;
+  const bool fp8 = kvkind == K_FP8;
+  if (p.D == 64) {
+    if (qkind == K_F16)
+      return fp8 ? launch_one<K_F16, K_FP8, 64, PFX>(p, stream) : launch_one<K_F16, K_F16, 64, PFX>(p, stream);
+    return fp8 ? launch_one<K_BF16, K_FP8, 64, PFX>(p, stream) : launch_one<K_BF16, K_BF16, 64, PFX>(p, stream);
+  }
+  if (qkind == K_F16)
+    return fp8 ? launch_one<K_F16, K_FP8, 128, PFX>(p, stream) : launch_one<K_F16, K_F16, 128, PFX>(p, stream);
+  return fp8 ? launch_one<K_BF16, K_FP8, 128, PFX>(p, stream) : launch_one<K_BF16, K_BF16, 128, PFX>(p, stream);
 }
 
 }  // namespace
@@ -424,14 +505,11 @@ bool prefill_variant_built(int qkind, int kvkind, int D) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
-  if (!prefill_variant_built(qkind, kvkind, p.D)) return hipErrorNotSupported;
-  const bool fp8 = kvkind == K_FP8;
-  if (p.D == 64) {
-    if (qkind == K_F16) return fp8 ? launch_one<K_F16, K_FP8, 64>(p, stream) : launch_one<K_F16, K_F16, 64>(p, stream);
-    return fp8 ? launch_one<K_BF16, K_FP8, 64>(p, stream) : launch_one<K_BF16, K_BF16, 64>(p, stream);
-  }
-  if (qkind == K_F16) return fp8 ? launch_one<K_F16, K_FP8, 128>(p, stream) : launch_one<K_F16, K_F16, 128>(p, stream);
-  return fp8 ? launch_one<K_BF16, K_FP8, 128>(p, stream) : launch_one<K_BF16, K_BF16, 128>(p, stream);
+  return launch_mode<false>(p, qkind, kvkind, stream);
+}
+
+hipError_t launch_prefix_pass(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
+  return launch_mode<true>(p, qkind, kvkind, stream);
 }
 
 }  // namespace pa

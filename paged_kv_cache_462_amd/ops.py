@@ -127,6 +127,39 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                            int(block_size), int(num_kv_heads), byref(ln)))
 
 
+def decode_shared_prefix_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int,
+                                         head_dim: int, block_size: int, max_blocks: int,
+                                         prefix_tokens: int) -> int:
+    return check(load().pa_decode_shared_prefix_workspace_bytes(
+        batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, prefix_tokens))
+
+
+def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, block_tables: torch.Tensor,
+                         seq_lens: torch.Tensor, prefix_blocks: torch.Tensor, prefix_tokens: int,
+                         scale: float, block_size: int, num_kv_heads: int,
+                         k_scale: float = 1.0, v_scale: float = 1.0,
+                         kv_dtype: Optional[str] = None,
+                         workspace: Optional[torch.Tensor] = None,
+                         stream: Optional[torch.cuda.Stream] = None) -> None:
+    """pa_decode_shared_prefix: decode of a batch whose sequences share their
+    first prefix_tokens tokens (the blocks in prefix_blocks).  Without a
+    workspace one is allocated here (torch owns it)."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    if workspace is None:
+        need = decode_shared_prefix_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
+                                                    query.shape[2], block_size,
+                                                    block_tables.shape[1], prefix_tokens)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+    args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
+            _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
+            _desc(prefix_blocks))
+    ln = _launch(query, workspace, 0, PATH_AUTO, stream)
+    check(load().pa_decode_shared_prefix(*(byref(a) for a in args), int(prefix_tokens),
+                                         ctypes.c_float(scale), int(block_size),
+                                         int(num_kv_heads), byref(ln)))
+
+
 def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
             value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
             query_start_loc: torch.Tensor, max_query_len: int, scale: float, block_size: int,

@@ -1,4 +1,4 @@
-"""The five paged-decode workloads, by shape.
+"""The paged-decode workloads, by shape.
 
 Shapes follow the paged layout [num_blocks, block_size, num_kv_heads,
 head_dim] used by the `paged_attention` code block of the page
@@ -93,6 +93,16 @@ _add(WorkloadConfig(
     batch=128, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=32,
     q_dtype="bf16", kv_dtype="fp8", lengths=("lognormal", 7.0, 1.0, 16, 16384),
     shared_prefix_tokens=1024, seed=1005))
+
+_add(WorkloadConfig(
+    name="shared_system_prompt_decode_bf16",
+    description="200 requests sharing a 512-token system prompt (32 ref-counted "
+                "blocks of 16), each with 16..256 tokens of its own after it "
+                "(seq_lens uniform in [528, 768]), 64 q / 8 kv heads, d=128, "
+                "bs=16, bf16",
+    batch=200, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+    q_dtype="bf16", kv_dtype="bf16", lengths=("uniform", 528, 768),
+    shared_prefix_tokens=512, seed=1006))
 
 # Ordered as listed above; index 0 is the small case, index 1 the bench case.
 CONFIG_ORDER = list(CONFIGS)
