@@ -431,6 +431,9 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   f.G = p.G;
   f.D = p.D;
   f.bs = p.bs;
+  f.T = p.B;
+  f.max_blocks = p.max_blocks;
+  f.num_blocks = p.num_blocks;
   f.spb_shift = -1;
   for (int sh = 0; sh < 24; ++sh)
     if ((16 << sh) == p.bs) f.spb_shift = sh;
@@ -585,6 +588,9 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   p.D = (int)D;
   p.bs = (int)bs;
   p.tile_ranks = (int)ranks;
+  p.T = (int)T;
+  p.max_blocks = (int)block_tables->shape[1];
+  p.num_blocks = (int)N;
   p.xcd_groups = (B * Hkv) % 8 == 0 ? (int)(B * Hkv / 8) : 0;
   p.spb_shift = -1;
   for (int sh = 0; sh < 24; ++sh)

@@ -20,6 +20,9 @@ struct PrefillParams {
   int64_t o_st, o_sh;     // output strides
   int64_t tab_stride;     // block-table row stride
   int32_t B, Hq, Hkv, G, D, bs;
+  int32_t T;              // query / output rows
+  int32_t max_blocks;     // block-table width (lengths are clamped to it)
+  int32_t num_blocks;     // pool size (ids outside it read block 0)
   int32_t tile_ranks;     // query-tile ranks in the grid (grid.x / (Hq * B))
   int32_t spb_shift;      // log2(bs / 16) when bs / 16 is a power of two, else -1
   int32_t xcd_groups;     // (sequence, kv head) groups per XCD when B * Hkv is a

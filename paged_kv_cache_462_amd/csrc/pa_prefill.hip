@@ -167,9 +167,11 @@ void prefill_mfma_kernel(PrefillParams p) {
     kvh = h / p.G;
   }
   // causal: rows of sequence b; prefix pass: all B * G (sequence, head) rows
-  const int q0 = PFX ? 0 : p.qsl[b];
-  const int n = PFX ? p.B * p.G : p.qsl[b + 1] - q0;
-  const int L = PFX ? p.pfx_tokens : p.lens[b];
+  // device-resident sizes are clamped to what the buffers hold (a value
+  // outside them is a caller error; clamping keeps every access in bounds)
+  const int q0 = PFX ? 0 : min(max(p.qsl[b], 0), p.T);
+  const int n = PFX ? p.B * p.G : min(p.qsl[b + 1], p.T) - q0;
+  const int L = PFX ? p.pfx_tokens : min(p.lens[b], p.max_blocks * p.bs);
   const int ntiles = (n + kBM - 1) / kBM;
   const int ctx = L - n;  // position of row 0 (negative when n > L)
   const int32_t* tab = p.tables + (int64_t)b * p.tab_stride;
@@ -213,7 +215,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       if constexpr (PFX) {
         // row = b * G + j: sequence b, query head kvh * G + j
         const int rb = rc / p.G;
-        pos[qs] = row < n ? min(max(p.lens[rb], 0), L) - 1 : -1;
+        pos[qs] = row < n ? min(max(p.lens[rb], 0), L) - 1 : -1;  // L <= the table's reach
         qoff = (int64_t)rb * p.q_st + (int64_t)(h + rc - rb * p.G) * p.q_sh;
       } else {
         pos[qs] = ctx + row;
@@ -260,7 +262,8 @@ void prefill_mfma_kernel(PrefillParams p) {
     // ahead, so reading an id (v_readlane) never waits on the table
     auto fetch_ids = [&](int chunk) {
       const int tok0 = (chunk * 64 + lane) * 16;
-      return tok0 < kv_end ? tab[tok0 / p.bs] : 0;
+      const int id = tok0 < kv_end ? tab[tok0 / p.bs] : 0;
+      return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
     };
     int ids_cur = fetch_ids(kt0 >> 4), ids_nxt = fetch_ids((kt0 >> 4) + 1), ids_chunk = kt0 >> 4;
 
