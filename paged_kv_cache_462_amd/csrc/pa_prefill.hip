@@ -28,8 +28,8 @@
 //    256-byte row) into registers one tile ahead and stores them to a
 //    double-buffered LDS tile at the top of the next iteration (slots past
 //    the keys the tile needs are zeroed there, so a stale NaN never meets a
-//    zero weight).  LDS rows are padded to 272 bytes: 16 consecutive rows
-//    start on 16 different 16-byte bank groups.
+//    zero weight).  LDS rows are padded (K 272, V 288 bytes at head_dim
+//    128) so that the operand reads hit distinct banks.
 // Per wave and KV tile:
 //  * scores^T[16 keys x 16 rows] = K[16 x D] . Q^T[D x 16] on
 //    v_mfma_f32_16x16x32; Q stays in registers.  Lane l gets keys
@@ -114,19 +114,25 @@ void prefill_mfma_kernel(PrefillParams p) {
   constexpr bool BF = QK == K_BF16;
   constexpr int CH = D / 8;                      // 16-byte chunks (8 values) per row
   constexpr int DB = D / 16;                     // 16-dim output blocks
-  constexpr int kRowBytes = D * 2 + 16;          // LDS row: D 16-bit values + pad
+  // LDS row pitches (D 16-bit values + pad), chosen for the 64 four-byte
+  // banks: a K row starts 4 banks after the previous one, so the 16 rows a
+  // 16-lane group reads at one chunk (ds_read_b128) cover all 64 banks; a V
+  // row starts 8 banks after the previous one (D = 128; 40 for D = 64), so
+  // the 8 rows x 32 bytes that 32 lanes' transpose reads (ds_read_b64_tr_b16)
+  // cover do not overlap
+  constexpr int kRowK = D * 2 + 16;
+  constexpr int kRowV = D * 2 + 32;
   constexpr int kStageRows = kThreads / CH;      // KV-tile rows one staging pass covers
   constexpr int kStagePasses = kBN / kStageRows;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int ESZ = Esz<KVK>::v;
   constexpr int kOne2 = BF ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
   const i32x4 kOnes = i32x4{kOne2, kOne2, kOne2, kOne2};
-  // K and V tiles, double-buffered, rows padded to kRowBytes: 16
-  // consecutive rows start on 16 different 16-byte bank groups, so the
+  // K and V tiles, double-buffered, with the padded pitches above: the
   // operand reads below are conflict-free with plain (immediate-offset)
   // addressing
-  __shared__ __attribute__((aligned(16))) char k_lds[2][kBN * kRowBytes];
-  __shared__ __attribute__((aligned(16))) char v_lds[2][kBN * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char k_lds[2][kBN * kRowK];
+  __shared__ __attribute__((aligned(16))) char v_lds[2][kBN * kRowV];
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -189,8 +195,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   // LDS byte offsets this lane reads from: the K operand (row n16 of a key
   // subtile, chunk g of a k-step) and the V^T transpose source (row 4g +
   // n16/4 of a 4-key group, dims 4 (n16 % 4) .. +3 of a 16-dim block)
-  const int k_rd = n16 * kRowBytes + g * 16;
-  const int v_rd = (4 * g + (n16 >> 2)) * kRowBytes + (n16 & 3) * 8;
+  const int k_rd = n16 * kRowK + g * 16;
+  const int v_rd = (4 * g + (n16 >> 2)) * kRowV + (n16 & 3) * 8;
 
   // causal: heaviest tile first, looping when the grid has fewer ranks than
   // tiles; prefix pass: exactly row tile `rank`
@@ -302,8 +308,8 @@ void prefill_mfma_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < kStagePasses; ++i) {
           const int r = srow + kStageRows * i;
-          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowBytes + sch * 16]) = kr[i];
-          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowBytes + sch * 16]) = vr[i];
+          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowK + sch * 16]) = kr[i];
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) = vr[i];
         }
       } else {
         // the keys end inside this tile: slots past the sequence's end hold
@@ -313,8 +319,8 @@ void prefill_mfma_kernel(PrefillParams p) {
         for (int i = 0; i < kStagePasses; ++i) {
           const int r = srow + kStageRows * i;
           const bool live = key0 + r < kv_end;
-          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowBytes + sch * 16]) = live ? kr[i] : i32x4{0, 0, 0, 0};
-          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowBytes + sch * 16]) = live ? vr[i] : i32x4{0, 0, 0, 0};
+          *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowK + sch * 16]) = live ? kr[i] : i32x4{0, 0, 0, 0};
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) = live ? vr[i] : i32x4{0, 0, 0, 0};
         }
       }
       __syncthreads();
@@ -332,7 +338,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       for (int st = 0; st < KS; ++st) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const i32x4 kf = *reinterpret_cast<const i32x4*>(&k_lds[buf][k_rd + ks * 16 * kRowBytes + st * 64]);
+          const i32x4 kf = *reinterpret_cast<const i32x4*>(&k_lds[buf][k_rd + ks * 16 * kRowK + st * 64]);
 #pragma unroll
           for (int qs = 0; qs < kQSub; ++qs) s[qs][ks] = mfma_k32<BF>(kf, qf[qs][st], s[qs][ks]);
         }
@@ -414,9 +420,9 @@ void prefill_mfma_kernel(PrefillParams p) {
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int jb = 0; jb < DB; ++jb) {
-          const char* vp = &v_lds[buf][v_rd + s2 * 32 * kRowBytes + jb * 32];
+          const char* vp = &v_lds[buf][v_rd + s2 * 32 * kRowV + jb * 32];
           const i32x2 lo = lds_tr16(vp);
-          const i32x2 hi = lds_tr16(vp + 16 * kRowBytes);
+          const i32x2 hi = lds_tr16(vp + 16 * kRowV);
           const i32x4 a = i32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qs = 0; qs < kQSub; ++qs) {
