@@ -989,13 +989,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const DecodeParams
 }
 
 // Rows per merge workgroup from the expected pieces per row: the balanced
-// plan deals 256 shares over the batch (about 256 / B + 1 pieces per
-// sequence, plus the prefix pass's), the fixed plan splits long sequences
-// into num_parts.
+// plan deals nwc shares of each unit chunk over the batch (about nwc / B + 1
+// pieces per sequence, plus the prefix pass's), the fixed plan splits long
+// sequences into num_parts.
 template <int QK, int D>
 hipError_t launch_merge(const DecodeParams& p, hipStream_t stream) {
   const int pieces = p.sched == kSchedBalanced
-                         ? kBalancedWorkgroups / max(p.B, 1) + 1 + p.prefix_pieces
+                         ? p.nwc / max(p.B, 1) + 1 + p.prefix_pieces
                          : p.num_parts;
   const int rows = p.B * p.Hq;
   auto go = [&](auto rtag) {

@@ -189,6 +189,10 @@ void prefill_mfma_kernel(PrefillParams p) {
   // subtile (srow >> 4) + (kStageRows / 16) i is wave-uniform
   const int srow = threadIdx.x / CH;
   const int sch = threadIdx.x % CH;
+  // the wave's first staging subtile (srow >> 4 is the same for all its
+  // lanes), as a scalar, so the block lookups and K/V addresses below are
+  // scalar arithmetic with scalar branches
+  const int sub_w = __builtin_amdgcn_readfirstlane(srow >> 4);
   // a 16-token subtile lies in one block: uniform base + this per-lane part
   const uint32_t lane_off = (uint32_t)((srow & 15) * tok_bytes + sch * 8 * ESZ);
   const int64_t blk_bytes = (int64_t)p.bs * tok_bytes;
@@ -284,7 +288,7 @@ void prefill_mfma_kernel(PrefillParams p) {
       }
 #pragma unroll
       for (int i = 0; i < kStagePasses; ++i) {
-        const int sub = kt * 4 + (srow >> 4) + (kStageRows / 16) * i;  // wave-uniform
+        const int sub = kt * 4 + sub_w + (kStageRows / 16) * i;
         const int sub0 = sub * 16;
         if (sub0 < kv_end) {
           const int blk = __builtin_amdgcn_readlane(ids_cur, sub & 63);
