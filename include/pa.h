@@ -126,7 +126,9 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
  *   value_cache   [N, bs, Hkv, D] contiguous; dtype of query, or PA_FP8_E4M3
  *                               with per-tensor `scale` (f16 / bf16 query)
  *   block_tables  [B, max_blocks] i32, column stride 1, entries past
- *                               ceil(seq_lens[b] / bs) are never read
+ *                               ceil(seq_lens[b] / bs) are never read;
+ *                               max_blocks * bs <= 2^31 - 1
+ *                               (PA_ERR_UNSUPPORTED otherwise)
  *   seq_lens      [B]           i32, 0 <= seq_lens[b] <= max_blocks * bs;
  *                               a zero length gives a zero output row
  *   scale         score scale (1/sqrt(D) for standard attention)
@@ -170,7 +172,9 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
  *   value_cache     [N, bs, Hkv, D] contiguous; dtype of query, or
  *                                 PA_FP8_E4M3 with per-tensor `scale`
  *   block_tables    [B, max_blocks] i32, column stride 1; entries past
- *                                 ceil(seq_lens[b] / bs) are never read
+ *                                 ceil(seq_lens[b] / bs) are never read;
+ *                                 max_blocks * bs <= 2^30
+ *                                 (PA_ERR_INVALID_ARG otherwise)
  *   seq_lens        [B] i32, 0 <= seq_lens[b] <= max_blocks * bs
  *   query_start_loc [B + 1] i32 (device), query_start_loc[0] = 0, rising to
  *                                 query_start_loc[B] = T
