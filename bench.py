@@ -22,6 +22,9 @@ Prints ONE JSON line:
                   against the 8 TB/s HBM peak; `traffic` from the committed
                   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken
                   from the current kernel source, else null
+  cache_write     pa_reshape_and_cache timed on its own after the steps:
+                  the step's new token per sequence, and a bulk write of
+                  every token of the batch (GB/s over bytes read + written)
   cpu_baseline    the CPU oracle (fp64) on a bounded sample of the same
                   batch, on this host's cores, for context only
 """
@@ -465,6 +468,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=0,
                     help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
     ap.add_argument("--hot-iters", type=int, default=20)
+    ap.add_argument("--write-iters", type=int, default=20,
+                    help="pa_reshape_and_cache launches timed on their own, after the steps")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
     ap.add_argument("--time-every", type=int, default=4,
@@ -481,7 +486,7 @@ def main() -> int:
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "the decode path shards by kv head or by sequence with no exchange inside attention, "
-              "and multi-GPU runs are not part of this build.", file=sys.stderr)
+              "and the library has no multi-GPU launch to measure.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -603,8 +608,49 @@ def main() -> int:
         decode(0)
         timer.record(b, stream)
         hot_ms.append(timer.elapsed_ms(a, b))
+    # pa_reshape_and_cache on its own, after the timed steps: the step's new
+    # token per sequence, and a bulk write of every token of the batch (the
+    # cache fill), each launch between two events.  A decode call is queued
+    # in front of each, so the host has enqueued the write before the GPU
+    # reaches it and the events time the kernel, not the host's launch.
+    def timed(fn, layer):
+        a, b = timer.create(), timer.create()
+        decode(layer)
+        timer.record(a, stream)
+        fn()
+        timer.record(b, stream)
+        return timer.elapsed_ms(a, b)
+
+    wr_step_ms = [timed(lambda: write(i % n_layers), (i + 1) % n_layers)
+                  for i in range(args.write_iters)]
+    wr_bulk_ms = []
+    if args.write_iters:
+        all_k, all_v = wl.tok_key.to(dev), wl.tok_value.to(dev)
+        all_s = torch.from_numpy(wl.slot_mapping).to(dev)
+        for i in range(3):
+            k_, v_ = layers[i % n_layers]
+            wr_bulk_ms.append(timed(lambda: pa.reshape_and_cache(
+                all_k, all_v, all_s, k_, v_, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                kv_dtype=kvd), (i + 1) % n_layers))
+        del all_k, all_v, all_s
     timer.close()
     hot_med = float(np.median(hot_ms)) if hot_ms else None
+    # bytes a write moves per token: K and V read in the source dtype and
+    # written in the cache dtype, plus its slot
+    tok_bytes = 2 * c.num_kv_heads * c.head_dim * (wl.tok_key.element_size() + kc.element_size()) + 8
+    cache_write = None
+    if wr_step_ms:
+        step_us = float(np.median(wr_step_ms)) * 1e3
+        bulk_ms = float(np.median(wr_bulk_ms))
+        cache_write = {
+            "kernel": "pa_reshape_and_cache",
+            "step_tokens": int((wl.new_slots >= 0).sum()),
+            "step_median_us": round(step_us, 2),
+            "bulk_tokens": wl.num_tokens,
+            "bulk_median_ms": round(bulk_ms, 4),
+            "bulk_GBps": round(wl.num_tokens * tok_bytes / (bulk_ms * 1e-3) / 1e9, 1),
+            "bytes_per_token": tok_bytes,
+        }
 
     kv_unique = wl.unique_kv_bytes()
     kv_logical = wl.logical_kv_bytes()
@@ -663,6 +709,7 @@ def main() -> int:
         "pct_of_hbm_peak": round(100 * gbps_step / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(c.batch / (ms_step * 1e-3), 1),
         "roofline": roof,
+        "cache_write": cache_write,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

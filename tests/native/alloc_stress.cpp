@@ -13,7 +13,8 @@
 #include "pa.h"
 
 // pa_alloc.cpp reports errors through this hook (the library's own lives
-// in the device-side translation unit, which this build leaves out).
+// in the C-ABI translation unit, which this host-only program does not
+// link).
 namespace pa {
 int set_error(int code, const char*) { return code; }
 }  // namespace pa
