@@ -127,8 +127,8 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value,
  *                               with per-tensor `scale` (f16 / bf16 query)
  *   block_tables  [B, max_blocks] i32, column stride 1, entries past
  *                               ceil(seq_lens[b] / bs) are never read;
- *                               max_blocks * bs <= 2^31 - 1
- *                               (PA_ERR_UNSUPPORTED otherwise)
+ *                               max_blocks * bs <= 2^30
+ *                               (PA_ERR_INVALID_ARG otherwise)
  *   seq_lens      [B]           i32, 0 <= seq_lens[b] <= max_blocks * bs;
  *                               a zero length gives a zero output row
  *   scale         score scale (1/sqrt(D) for standard attention)

@@ -185,10 +185,6 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   const int64_t max_blocks = block_tables->shape[1];
   if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "batch above 65535");
   if (N > 0x7FFFFFFFLL || max_blocks > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "pool or table too large");
-  // lengths are int32: a table row reaching past 2^31 - 1 tokens has no use,
-  // and the kernels clamp lengths to max_blocks * bs in 32-bit arithmetic
-  if (max_blocks * bs > 0x7FFFFFFFLL)
-    return fail(PA_ERR_UNSUPPORTED, "block table addresses more than 2^31 - 1 tokens");
   if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
   const int qes = elem_size(qdt);
   const int64_t vec = 16 / qes;

@@ -118,16 +118,16 @@ def test_decode_rejects(mut, code):
     _expect(_call_decode(a), code)
 
 
-def test_decode_rejects_table_past_int32_tokens():
-    # 2^27 blocks of 16 tokens: 2^31 token positions, one past what int32
-    # lengths reach (the descriptor is never dereferenced)
-    a = _decode_args(B=1, mb=1 << 27)
-    _expect(_call_decode(a), _lib.PA_ERR_UNSUPPORTED)
-    assert "2^31" in _lib.last_error()
-    a = _decode_args(B=1, mb=(1 << 27) - 1)
-    a["lens"] = _t([1], _lib.PA_I32)
-    rc = _call_decode(a)
-    assert rc != _lib.PA_ERR_UNSUPPORTED or "2^31" not in _lib.last_error()
+def test_decode_table_reach_limit():
+    # 2^26 blocks of 16 tokens address 2^30 token positions, the most a table
+    # may reach; one block more is rejected (descriptors never dereferenced)
+    a = _decode_args(B=1, mb=(1 << 26) + 1)
+    _expect(_call_decode(a), _lib.PA_ERR_INVALID_ARG)
+    assert "too many tokens" in _lib.last_error()
+    # at the limit the call passes validation and, with the automatic plan
+    # (which splits), stops at the missing workspace, before any launch
+    a = _decode_args(B=1, mb=1 << 26)
+    _expect(_call_decode(a, PaLaunch(None, None, 0, 0, 0)), _lib.PA_ERR_WORKSPACE)
 
 
 def test_decode_needs_workspace_when_split():
