@@ -130,8 +130,8 @@ class HipTimingEvents:
 
 
 def cpu_baseline(wl, seconds: float):
-    """The oracle, unchanged, over the first sequences of the batch until the
-    time budget is spent."""
+    """The oracle, unchanged, over the sequences of the batch in order (from
+    the first again after the last) until the time budget is spent."""
     import numpy as np
 
     from oracle import attention as OA
@@ -144,7 +144,8 @@ def cpu_baseline(wl, seconds: float):
     c = wl.cfg
     done, t_used, kv_bytes = 0, 0.0, 0
     esz = wl.kv_bytes_per_elem()
-    for b in range(c.batch):
+    while True:
+        b = done % c.batch
         pairs = [(b, h) for h in range(c.num_q_heads)]
         t0 = time.perf_counter()
         OA.paged_decode_stored(wl.query, kc, vc, c.kv_dtype, wl.k_scale, wl.v_scale,
@@ -167,9 +168,9 @@ def cpu_baseline(wl, seconds: float):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 oracle decode of sequences 0..{done - 1} of {c.batch} "
-                  f"(all {c.num_q_heads} query heads, {kv_bytes / 1e6:.1f} MB of KV) in "
-                  f"{t_used:.2f} s; tokens/s {done / t_used:.2f}",
+        "sample": f"fp64 oracle decode of {done} sequences ({done / c.batch:.1f} passes over the "
+                  f"batch of {c.batch}, all {c.num_q_heads} query heads, {kv_bytes / 1e6:.1f} MB "
+                  f"of KV) in {t_used:.2f} s; tokens/s {done / t_used:.2f}",
     }
 
 
