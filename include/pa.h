@@ -38,7 +38,11 @@
  *     and touches no device state.  Device-resident contents (block ids,
  *     lengths, slots) are trusted: block ids must lie in [0, num_blocks),
  *     seq_lens[b] <= max_blocks * block_size, slots must be unique and inside
- *     the cache.
+ *     the cache.  A violation gives unspecified values in the outputs it
+ *     touches, but every access stays inside the buffers of the call: a
+ *     block id outside the pool reads block 0, a length is clamped to
+ *     [0, max_blocks * block_size], a slot outside the cache is skipped and
+ *     query_start_loc entries are clamped to [0, T].
  *   - Every call returns PA_OK (0) or a negative status; pa_last_error()
  *     then holds a message (thread-local, valid until the next call on the
  *     same thread).
