@@ -67,6 +67,8 @@ namespace pa {
 namespace {
 
 constexpr int kTile = 16;
+// Lazy-rescale threshold of the matrix-core loop (log2 units).
+constexpr float kLazyLog2 = 8.0f;
 constexpr int kMaxWaves = 8;
 constexpr int kMaxThreads = kMaxWaves * 64;
 
@@ -394,7 +396,6 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
   constexpr int NJQ = D / 32;          // score MFMAs per tile (K = 32 dims each)
   constexpr int NJV = D / 16;          // P x V MFMAs per tile; V elements per lane per token
   constexpr int VBYTES = NJV * ESZ;    // V bytes per lane per token
-  constexpr int VW = NJV / 2;          // V words per token after conversion to 16-bit
   constexpr int SLOTS = kTile * LR;    // 16-byte LDS slots per tile
   static_assert(NK >= 1 && NR >= 1 && (kFP8 ? 2 * NR == NJQ : NR == NJQ), "shape");
   static_assert(VBYTES == 16 || VBYTES == 8 || VBYTES == 4, "shape");
@@ -486,6 +487,8 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
 
     auto compute_tile = [&](int i, Regs& r) {
       const int t0 = wk.t_lo + kTile * i;
+      // only a piece's last tile can reach past its end (wave-uniform)
+      const bool partial = t0 + kTile > wk.t_hi;
       // scores: D[token 4g+q][head n]
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -504,15 +507,31 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
       }
       float sv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        sv[q] = (t0 + 4 * g + q < wk.t_hi) ? s[q] * p.qk_scale_log2 : -INFINITY;
+      for (int q = 0; q < 4; ++q) sv[q] = s[q] * p.qk_scale_log2;
+      if (partial) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (t0 + 4 * g + q >= wk.t_hi) sv[q] = -INFINITY;
+      }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Lazy rescale: the weights are taken against a reference m that
+      // moves (rescaling the sum and the output by 2^(m - m_new)) only when
+      // some head's maximum passes it by more than 2^kLazyLog2, so the
+      // weights stay below 2^kLazyLog2 and most tiles skip the rescale.
+      // The result acc / l, and any merge of (m, l, acc) triples, is the
+      // same for every choice of reference.
       const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
-      const float p0 = fast_exp2(sv[0] - m_new), p1 = fast_exp2(sv[1] - m_new);
-      const float p2 = fast_exp2(sv[2] - m_new), p3 = fast_exp2(sv[3] - m_new);
+      if (__builtin_amdgcn_ballot_w64(m_new > m + kLazyLog2) != 0) {
+        const float alpha = fast_exp2(m - m_new);
+#pragma unroll
+        for (int j = 0; j < NJV; ++j) acc[j] = acc[j] * alpha;
+        l *= alpha;
+        m = m_new;
+      }
+      const float p0 = fast_exp2(sv[0] - m), p1 = fast_exp2(sv[1] - m);
+      const float p2 = fast_exp2(sv[2] - m), p3 = fast_exp2(sv[3] - m);
       // P as the B operand of the P x V MFMAs.  fp16 (11-bit significand)
       // is precise enough on its own; bf16 (8 bits) would put errors of
       // 2^-9 |v| on outputs whose terms nearly cancel, so there P goes in
@@ -532,44 +551,57 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
       } else {
         ps = (f16_lo(pw0) + f16_hi(pw0)) + (f16_lo(pw1) + f16_hi(pw1));
       }
-      l = l * alpha + ps;
-      m = m_new;
+      l += ps;
       const i32x2 pop = {(int)pw0, (int)pw1};
 
-      // V rows as 16-bit words: vw[q][k] holds elements 2k, 2k+1 of token
-      // 4g+q.  Tokens past the end of the sequence may hold anything (NaN
-      // poison): their rows are replaced by zeros (a select, not a branch,
-      // so the loads still in flight are not waited for) before P x V.
-      uint32_t vw[4][VW];
+      // V^T operand words of MFMA j: a0[j] = element j of tokens 4g, 4g+1,
+      // a1[j] = of tokens 4g+2, 4g+3.  Tokens past the end of the sequence
+      // may hold anything (NaN poison): on a partial tile their rows are
+      // replaced by zeros before P x V.
+      uint32_t rw[4][VBYTES / 4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool ok = t0 + 4 * g + q < wk.t_hi;
-        if constexpr (kFP8) {
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int k = 0; k < VW / 2; ++k) {
-            const i32x2 c2 = kBF16 ? fp8x4_to_bf16x4(r.v[q].w(k)) : fp8x4_to_f16x4(r.v[q].w(k));
-            vw[q][2 * k] = ok ? (uint32_t)c2[0] : 0u;
-            vw[q][2 * k + 1] = ok ? (uint32_t)c2[1] : 0u;
+        for (int k = 0; k < VBYTES / 4; ++k) rw[q][k] = r.v[q].w(k);
+      if (partial) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = t0 + 4 * g + q < wk.t_hi;
+#pragma unroll
+          for (int k = 0; k < VBYTES / 4; ++k) rw[q][k] = ok ? rw[q][k] : 0u;
+        }
+      }
+      uint32_t a0[NJV], a1[NJV];
+      if constexpr (kFP8) {
+        // interleave the two tokens' fp8 bytes, then convert pairs: one
+        // byte select and two conversions give four operand words
+#pragma unroll
+        for (int k = 0; k < VBYTES / 4; ++k) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t sel = h ? 0x07030602u : 0x05010400u;
+            const uint32_t x0 = __builtin_amdgcn_perm(rw[1][k], rw[0][k], sel);
+            const uint32_t x1 = __builtin_amdgcn_perm(rw[3][k], rw[2][k], sel);
+            const i32x2 c0 = kBF16 ? fp8x4_to_bf16x4(x0) : fp8x4_to_f16x4(x0);
+            const i32x2 c1 = kBF16 ? fp8x4_to_bf16x4(x1) : fp8x4_to_f16x4(x1);
+            a0[4 * k + 2 * h] = (uint32_t)c0[0];
+            a0[4 * k + 2 * h + 1] = (uint32_t)c0[1];
+            a1[4 * k + 2 * h] = (uint32_t)c1[0];
+            a1[4 * k + 2 * h + 1] = (uint32_t)c1[1];
           }
-        } else {
+        }
+      } else {
 #pragma unroll
-          for (int k = 0; k < VW; ++k) vw[q][k] = ok ? r.v[q].w(k) : 0u;
+        for (int j = 0; j < NJV; ++j) {
+          const int k = j >> 1;
+          a0[j] = (j & 1) ? pack_hi_halves(rw[0][k], rw[1][k]) : pack_lo_halves(rw[0][k], rw[1][k]);
+          a1[j] = (j & 1) ? pack_hi_halves(rw[2][k], rw[3][k]) : pack_lo_halves(rw[2][k], rw[3][k]);
         }
       }
 #pragma unroll
       for (int j = 0; j < NJV; ++j) {
-        const int k = j >> 1;
-        uint32_t a0, a1;
-        if (j & 1) {
-          a0 = pack_hi_halves(vw[0][k], vw[1][k]);
-          a1 = pack_hi_halves(vw[2][k], vw[3][k]);
-        } else {
-          a0 = pack_lo_halves(vw[0][k], vw[1][k]);
-          a1 = pack_lo_halves(vw[2][k], vw[3][k]);
-        }
-        acc[j] = acc[j] * alpha;
-        acc[j] = mfma_k16<kBF16>(i32x2{(int)a0, (int)a1}, pop, acc[j]);
-        if constexpr (kBF16) acc[j] = mfma_k16<kBF16>(i32x2{(int)a0, (int)a1}, pop_lo, acc[j]);
+        acc[j] = mfma_k16<kBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop, acc[j]);
+        if constexpr (kBF16) acc[j] = mfma_k16<kBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop_lo, acc[j]);
       }
     };
 
