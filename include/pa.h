@@ -297,9 +297,11 @@ typedef struct pa_decode_plan_info {
 
 /*
  * The plan pa_decode makes for these sizes and this partition request:
- * partition_tokens 0 (automatic) picks the balanced schedule when
- * batch <= 2048, else 512-token partitions; -1 never splits; > 0 asks for
- * partitions of that many tokens.  Returns PA_OK or a negative status.
+ * partition_tokens 0 (automatic) runs one pass per sequence (no split) when
+ * the block table reaches at most 256 tokens (max_blocks * block_size), else
+ * picks the balanced schedule when batch <= 2048, else 512-token
+ * partitions; -1 never splits; > 0 asks for partitions of that many tokens.
+ * Returns PA_OK or a negative status.
  */
 int pa_decode_plan(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                    int32_t head_dim, int32_t block_size, int32_t max_blocks,

@@ -105,7 +105,15 @@ struct Plan {
 // reads seq_lens (they live on the device): the balanced schedule finds the
 // lengths on the device, and a fixed split covers the table width (its
 // partitions past a sequence's end exit at once).
-int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out) {
+// Contexts this short (every sequence within 256 tokens, 16 tiles) run in
+// one pass under the automatic plan: a workgroup per (sequence, unit
+// chunk) walks them in about the time a second (merge) launch would take.
+constexpr int kSinglePassMaxTokens = 256;
+
+// balanced_only: the automatic plan is always the balanced schedule (the
+// shared-prefix decode needs it), whatever the context length.
+int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out,
+              bool balanced_only = false) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0)
     return fail(PA_ERR_INVALID_ARG, "sizes must be positive");
   if (Hq % Hkv) return fail(PA_ERR_INVALID_ARG, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", Hq, Hkv);
@@ -118,7 +126,9 @@ int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Pl
   if (req < -1) return fail(PA_ERR_INVALID_ARG, "partition_tokens must be -1, 0 or positive");
   Plan p;
   const int64_t max_tiles = (int64_t)B * ((max_ctx + 15) / 16);
-  if (req == 0 && B <= pa::kBalancedMaxBatch && max_tiles < (int64_t)1 << 30) {
+  if (req == 0 && !balanced_only && max_ctx <= kSinglePassMaxTokens) {
+    p.part_tokens = max_ctx > 0 ? ((max_ctx + 15) / 16) * 16 : 16;
+  } else if (req == 0 && B <= pa::kBalancedMaxBatch && max_tiles < (int64_t)1 << 30) {
     // automatic: equal shares of the batch's tiles per workgroup
     p.sched = pa::kSchedBalanced;
     p.split = 1;
@@ -149,7 +159,8 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
                  const pa_tensor* value_cache, const pa_tensor* block_tables,
                  const pa_tensor* seq_lens, float scale, int32_t block_size,
                  int32_t num_kv_heads, const pa_launch* launch, int64_t extra_ws_bytes,
-                 pa::DecodeParams* out_p, pa::DecodeVariant* out_v, Plan* out_plan, bool* empty) {
+                 pa::DecodeParams* out_p, pa::DecodeVariant* out_v, Plan* out_plan, bool* empty,
+                 bool balanced_only = false) {
   *empty = false;
   int rc;
   if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(out, "out", 3)) ||
@@ -194,7 +205,7 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
     return fail(PA_ERR_INVALID_ARG, "out rows must be 16-byte aligned");
   Plan plan;
   if ((rc = make_plan((int)B, (int)Hq, (int)Hkv, (int)D, (int)bs, (int)max_blocks,
-                      launch ? launch->partition_tokens : 0, &plan)))
+                      launch ? launch->partition_tokens : 0, &plan, balanced_only)))
     return rc;
   const int G = (int)(Hq / Hkv);
   const int req_path = launch ? launch->path : PA_PATH_AUTO;
@@ -357,7 +368,8 @@ int64_t pa_decode_shared_prefix_workspace_bytes(int32_t batch, int32_t num_q_hea
                                                 int32_t block_size, int32_t max_blocks,
                                                 int32_t prefix_tokens) {
   Plan p;
-  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, 0, &p);
+  int rc = make_plan(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks, 0, &p,
+                     true);
   if (rc) return rc;
   if (p.sched != pa::kSchedBalanced)
     return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode takes batches of at most %d",
@@ -395,7 +407,8 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   Plan plan;
   bool empty;
   if ((rc = decode_setup(out, query, key_cache, value_cache, block_tables, seq_lens, scale, block_size,
-                         num_kv_heads, &ln, pp.extra_ws_bytes, &p, &v, &plan, &empty)))
+                         num_kv_heads, &ln, pp.extra_ws_bytes, &p, &v, &plan, &empty,
+                         true)))
     return rc;
   if (plan.sched != pa::kSchedBalanced)
     return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode takes batches of at most %d",

@@ -5,6 +5,8 @@ path / partition choice; full-size cases run in the benchmark's launch
 configuration and compare sampled rows.  Cache writes are compared bit for
 bit."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -300,6 +302,17 @@ def test_full_size(name):
 
 # --- the balanced schedule (automatic plan) -------------------------------------
 
+def _wide_table(wl, tokens=512):
+    """The same workload with its block table padded (-1) to address at
+    least `tokens` tokens, so that the automatic plan is the balanced
+    schedule even for short sequences (tables reaching at most 256 tokens
+    run in one pass)."""
+    bs = wl.cfg.block_size
+    extra = max(0, -(-tokens // bs) - wl.max_blocks)
+    tables = np.pad(wl.block_tables, ((0, 0), (0, extra)), constant_values=-1)
+    return dataclasses.replace(wl, block_tables=tables)
+
+
 def _random_lengths(B, hi, seed, zero_frac=0.1):
     rng = np.random.default_rng(seed)
     L = rng.integers(1, hi + 1, B)
@@ -313,7 +326,7 @@ def test_balanced_many_sequences(name):
     boundary pattern of the balanced schedule, against the oracle."""
     lens = _random_lengths(300, 200, seed=11)
     cfg = shrink(get_config(name), batch=300, lengths=("list", lens))
-    wl = make_workload(cfg, seed=12)
+    wl = _wide_table(make_workload(cfg, seed=12))
     plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                           cfg.block_size, wl.max_blocks, 0)
     assert plan["schedule"] == "balanced"
@@ -335,7 +348,7 @@ def test_balanced_batch_limit(B, schedule):
     pass per sequence)."""
     lens = _random_lengths(B, 40, seed=B)
     cfg = shrink(get_config("c3"), batch=B, lengths=("list", lens))
-    wl = make_workload(cfg, seed=13)
+    wl = _wide_table(make_workload(cfg, seed=13))
     plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
                           cfg.block_size, wl.max_blocks, 0)
     assert plan["schedule"] == schedule
@@ -349,6 +362,35 @@ def test_balanced_batch_limit(B, schedule):
     ref = G.oracle_decode(wl, kc, vc, pairs)
     atol, rtol = G.tol_for(wl)
     G.assert_close(out, ref, atol, rtol, pairs=pairs, what=f"batch limit B={B}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
+def test_short_context_single_pass(name):
+    """Tables that reach at most 256 tokens: the automatic plan is one pass
+    per sequence with no workspace, it matches the oracle, and it matches
+    the balanced schedule on the same data with a wider table."""
+    lens = {"c1": [100], "c2": [1, 16, 17, 255, 256, 0], "c3": [256, 5, 130],
+            "c5": [32, 200, 256, 7]}[name]
+    cfg = shrink(get_config(name), batch=len(lens), lengths=("list", lens))
+    wl = make_workload(cfg, seed=21)
+    plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                          cfg.block_size, wl.max_blocks, 0)
+    assert plan["schedule"] == "single" and plan["workspace_bytes"] == 0
+    wide = _wide_table(wl)
+    plan = pa.decode_plan(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                          cfg.block_size, wide.max_blocks, 0)
+    assert plan["schedule"] == "balanced"
+    G.say(f"short context single pass {name}")
+    kc, vc = G.oracle_caches(wl)
+    d = G.to_device(wl)
+    a = G.gpu_decode(wl, d, partition_tokens=0)
+    d.tables = torch.from_numpy(wide.block_tables).to(d.tables.device)
+    b = G.gpu_decode(wide, d, partition_tokens=0)
+    torch.cuda.synchronize()
+    ref = G.oracle_decode(wl, kc, vc)
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(a, ref, atol, rtol, what=f"short single {name}")
+    G.assert_close(b, ref, atol, rtol, what=f"short balanced {name}")
 
 
 @pytest.mark.parametrize("name", ["c2", "c4", "c5"])

@@ -170,6 +170,14 @@ def test_plan():
     assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_PARTITIONS and info.partition_tokens == 1024
     rc, info = _plan(32, 32, 32, 128, 16, 32, 512)      # 512 tokens: one partition
     assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_SINGLE
+    # automatic with a table that reaches at most 256 tokens: one pass, no
+    # workspace; one block more and the balanced schedule
+    for mb, bs in ((16, 16), (7, 16), (8, 32), (0, 16)):
+        rc, info = _plan(64, 32, 8, 128, bs, mb, 0)
+        assert rc == 0 and info.schedule == _lib.PA_SCHEDULE_SINGLE and info.workspace_bytes == 0
+        assert lib.pa_decode_workspace_bytes(64, 32, 8, 128, bs, mb, 0) == 0
+    rc, info = _plan(64, 32, 8, 128, 16, 17, 0)
+    assert rc == 0 and info.schedule == B_
     rc, _ = _plan(4, 32, 8, 128, 16, 2048, 100)
     assert rc == _lib.PA_ERR_INVALID_ARG
     assert lib.pa_decode_workspace_bytes(4, 32, 8, 128, 16, 2048, 512) == 4 * 32 * 64 * 130 * 4
