@@ -2,7 +2,7 @@
 
 Small cases span several 16-token tiles with ragged tails and run every
 path / partition choice; full-size cases run in the benchmark's launch
-configuration and compare sampled rows.  Cache writes are compared bit for
+configuration and compare every output element.  Cache writes are compared bit for
 bit."""
 
 import dataclasses
@@ -284,6 +284,9 @@ FULL = ["c1", "c2", "c3", "c4", "c5"]
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size(name):
+    """Every output of the full-size workload against the oracle (the error
+    summary printed here is the one the measured-results table quotes), and
+    the cache write bit for bit."""
     cfg = get_config(name)
     wl = make_workload(cfg)
     G.say(f"full {name}: B={cfg.batch} N={wl.num_blocks} T={wl.num_tokens}")
@@ -294,10 +297,15 @@ def test_full_size(name):
     assert G.caches_equal(d.kc, kc)
     assert G.caches_equal(d.vc, vc)
     del d
-    pairs = None if name == "c1" else G.sample_pairs(wl, 48)
-    ref = G.oracle_decode(wl, kc, vc, pairs)
+    ref = G.oracle_decode(wl, kc, vc)
     atol, rtol = G.tol_for(wl)
-    G.assert_close(out, ref, atol, rtol, pairs=pairs, what=f"full {name}")
+    g = out.to("cpu", torch.float64).numpy()
+    err = np.abs(g - ref)
+    big = np.abs(ref) > 1e-2
+    G.say(f"full {name}: {err.size} outputs, max abs err {err.max():.2e}, max rel err "
+          f"(|ref| > 0.01) {(err[big] / np.abs(ref[big])).max():.2e}, max err / bound "
+          f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")
+    G.assert_close(out, ref, atol, rtol, what=f"full {name}")
 
 
 # --- the balanced schedule (automatic plan) -------------------------------------
