@@ -42,7 +42,8 @@
  *     touches, but every access stays inside the buffers of the call: a
  *     block id outside the pool reads block 0, a length is clamped to
  *     [0, max_blocks * block_size], a slot outside the cache is skipped and
- *     query_start_loc entries are clamped to [0, T].
+ *     query_start_loc entries are clamped to [0, T].  A caller that wants
+ *     to know when that happened passes launch->error_flags (below).
  *   - Every call returns PA_OK (0) or a negative status; pa_last_error()
  *     then holds a message (thread-local, valid until the next call on the
  *     same thread).
@@ -97,7 +98,22 @@ typedef struct pa_launch {
                                split; > 0: split each sequence into partitions
                                of this many tokens (a multiple of 16)            */
   int32_t path;             /* PA_PATH_*                                         */
+  int32_t* error_flags;     /* NULL, or a device int32[PA_NUM_FLAGS] the caller
+                               has zeroed: a kernel that meets device-resident
+                               contents outside their contract and takes them
+                               the documented way (see the conventions above)
+                               stores 1 into the flag of that kind; flags are
+                               never cleared by the library.  Calls that
+                               overlap on one array may interleave their
+                               stores (each only ever stores 1)              */
 } pa_launch;
+
+/* error_flags entries (indices) */
+#define PA_FLAG_BLOCK_ID 0    /* a block id outside [0, num_blocks) was read   */
+#define PA_FLAG_LENGTH 1      /* a length outside [0, max_blocks * block_size] */
+#define PA_FLAG_SLOT 2        /* a cache-write slot >= num_blocks * block_size */
+#define PA_FLAG_QUERY_START 3 /* query_start_loc outside [0, T] or decreasing */
+#define PA_NUM_FLAGS 4
 
 /*
  * pa_reshape_and_cache -- write new K/V tokens into their cache slots.

@@ -6,7 +6,17 @@ tensors into the library's plain descriptors and calls it.  There is no
 fallback: if libpa.so is missing, every call raises.
 """
 
-from ._lib import LibraryMissing, PaError, lib_path, load  # noqa: F401
+from ._lib import (  # noqa: F401
+    PA_FLAG_BLOCK_ID,
+    PA_FLAG_LENGTH,
+    PA_FLAG_QUERY_START,
+    PA_FLAG_SLOT,
+    PA_NUM_FLAGS,
+    LibraryMissing,
+    PaError,
+    lib_path,
+    load,
+)
 from .ops import (  # noqa: F401
     PATH_AUTO,
     PATH_MFMA,

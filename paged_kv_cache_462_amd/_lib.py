@@ -43,10 +43,15 @@ class PaDecodePlan(ctypes.Structure):
 PA_SCHEDULE_SINGLE, PA_SCHEDULE_PARTITIONS, PA_SCHEDULE_BALANCED = 0, 1, 2
 
 
+# error_flags entries (indices into a device int32[PA_NUM_FLAGS])
+PA_FLAG_BLOCK_ID, PA_FLAG_LENGTH, PA_FLAG_SLOT, PA_FLAG_QUERY_START = 0, 1, 2, 3
+PA_NUM_FLAGS = 4
+
+
 class PaLaunch(ctypes.Structure):
     _fields_ = [("stream", c_void_p), ("workspace", c_void_p),
                 ("workspace_bytes", c_size_t), ("partition_tokens", c_int32),
-                ("path", c_int32)]
+                ("path", c_int32), ("error_flags", c_void_p)]
 
 
 _T = POINTER(PaTensor)

@@ -105,6 +105,14 @@ struct Plan {
 // reads seq_lens (they live on the device): the balanced schedule finds the
 // lengths on the device, and a fixed split covers the table width (its
 // partitions past a sequence's end exit at once).
+// The caller's error flags (launch->error_flags): null, or 4-byte aligned.
+int flags_of(const pa_launch* launch, int32_t** out) {
+  *out = launch ? launch->error_flags : nullptr;
+  if (*out && reinterpret_cast<uintptr_t>(*out) % 4)
+    return fail(PA_ERR_INVALID_ARG, "error_flags must be 4-byte aligned");
+  return PA_OK;
+}
+
 // Contexts this short (every sequence within 256 tokens, 16 tiles) run in
 // one pass under the automatic plan: a workgroup per (sequence, unit
 // chunk) walks them in about the time a second (merge) launch would take.
@@ -238,6 +246,7 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
 
   pa::DecodeParams p;
   memset(&p, 0, sizeof p);
+  if ((rc = flags_of(launch, &p.flags))) return rc;
   p.out = out->data;
   p.q = query->data;
   p.kc = key_cache->data;
@@ -430,6 +439,7 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
 
   pa::PrefillParams f;
   memset(&f, 0, sizeof f);
+  f.flags = p.flags;
   f.q = query->data;
   f.kc = key_cache->data;
   f.vc = value_cache->data;
@@ -498,6 +508,8 @@ int pa_reshape_and_cache(const pa_tensor* key, const pa_tensor* value, const pa_
   if (T == 0) return PA_OK;
   pa::CacheWriteParams p;
   memset(&p, 0, sizeof p);
+  int frc = flags_of(launch, &p.flags);
+  if (frc) return frc;
   p.key = key->data;
   p.value = value->data;
   p.slots = static_cast<const int64_t*>(slot_mapping->data);
@@ -582,6 +594,8 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   if (ranks * per_rank > (1LL << 24)) ranks = (1LL << 24) / per_rank > 0 ? (1LL << 24) / per_rank : 1;
   pa::PrefillParams p;
   memset(&p, 0, sizeof p);
+  int frc = flags_of(launch, &p.flags);
+  if (frc) return frc;
   p.out = out->data;
   p.q = query->data;
   p.kc = key_cache->data;
@@ -642,6 +656,8 @@ int launch_block_copy(const pa_tensor* dk, const pa_tensor* dv, const pa_tensor*
                       const pa_tensor* sv, const pa_tensor* pairs, int64_t bytes,
                       const pa_launch* launch, const char* what) {
   pa::CopyBlocksParams p;
+  int frc = flags_of(launch, &p.flags);
+  if (frc) return frc;
   p.src_k = sk->data;
   p.src_v = sv->data;
   p.dst_k = dk->data;

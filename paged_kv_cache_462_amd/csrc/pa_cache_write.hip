@@ -74,7 +74,11 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(const CacheWriteP
   const int64_t t = i / chunks;
   const int64_t c = i - t * chunks;
   const int64_t slot = p.slots[t];
-  if (slot < 0 || slot >= p.num_slots) return;
+  if (slot < 0) return;
+  if (slot >= p.num_slots) {
+    raise_flag(p.flags, kFlagSlot);
+    return;
+  }
   const int64_t dst = slot * row + c * kElemsPerThread;
   const int64_t ks = t * p.k_stride_tok + c * kElemsPerThread;
   const int64_t vs = t * p.v_stride_tok + c * kElemsPerThread;
@@ -116,7 +120,10 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(const CopyBlocksP
   const int64_t c = i - pair * chunks;
   const int64_t src = p.pairs[2 * pair];
   const int64_t dst = p.pairs[2 * pair + 1];
-  if (src < 0 || dst < 0 || src >= p.src_blocks || dst >= p.dst_blocks) return;
+  if (src < 0 || dst < 0 || src >= p.src_blocks || dst >= p.dst_blocks) {
+    raise_flag(p.flags, kFlagBlockId);
+    return;
+  }
   const int64_t so = src * p.block_bytes + c * 16;
   const int64_t d_o = dst * p.block_bytes + c * 16;
   const i32x4 k = *reinterpret_cast<const i32x4*>(static_cast<const char*>(p.src_k) + so);

@@ -123,6 +123,7 @@ __device__ __forceinline__ void store_f32_vec(float* dst, const float* x) {
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   const int L = p.lens[b];
   const int cap = p.max_blocks * p.bs;
+  if (L < 0 || L > cap) raise_flag(p.flags, kFlagLength);
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
@@ -252,7 +253,10 @@ __device__ __forceinline__ int load_block_ids(const DecodeParams& p, const Work&
     id = p.tables[(int64_t)wk.b * p.tab_stride + t / p.bs];
     // an id outside the pool is a caller error; read block 0 instead of
     // faulting
-    if ((unsigned)id >= (unsigned)p.num_blocks) id = 0;
+    if ((unsigned)id >= (unsigned)p.num_blocks) {
+      raise_flag(p.flags, kFlagBlockId);
+      id = 0;
+    }
   }
   return id;
 }

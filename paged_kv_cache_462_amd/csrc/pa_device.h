@@ -124,6 +124,14 @@ __device__ __forceinline__ f32x4 mfma_k16(i32x2 a, i32x2 b, f32x4 c) {
         __builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// ---- caller-visible error flags ------------------------------------------------
+// Flag k of the caller's array (null: none) is set to 1 when a kernel takes
+// device-resident contents outside their contract; a plain store, so any
+// number of lanes may set it at once.
+__device__ __forceinline__ void raise_flag(int32_t* flags, int k) {
+  if (flags) flags[k] = 1;
+}
+
 // ---- loads ----------------------------------------------------------------------
 template <int BYTES>
 struct Bytes;

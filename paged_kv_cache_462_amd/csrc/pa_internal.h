@@ -16,6 +16,11 @@ enum Kind : int { K_F32 = 0, K_F16 = 1, K_BF16 = 2, K_FP8 = 3 };
 // may cover the end of one sequence and the start of the next.
 enum Sched : int { kSchedFixed = 0, kSchedBalanced = 1 };
 
+// Caller's error flags (the launch's error_flags): index of the flag a
+// kernel sets to 1 when it takes device-resident contents outside their
+// contract the documented way (same order as the C ABI's PA_FLAG_*).
+enum Flag : int { kFlagBlockId = 0, kFlagLength = 1, kFlagSlot = 2, kFlagQueryStart = 3, kNumFlags = 4 };
+
 // Balanced schedule limits: workgroups per unit chunk (the workspace is
 // sized for this many) and the largest batch it takes (the per-sequence
 // tile offsets live in LDS).
@@ -56,6 +61,7 @@ struct DecodeParams {
   int32_t skip;
   int32_t prefix_pieces;
   int32_t prefix_slot0;
+  int32_t* flags;         // caller's error flags [kNumFlags], or null
 };
 
 struct DecodeVariant {
@@ -82,6 +88,7 @@ struct CacheWriteParams {
   int32_t Hkv, D, bs;
   int64_t num_slots;      // N * bs (slots beyond are ignored)
   float k_scale, v_scale; // fp8 caches
+  int32_t* flags;         // caller's error flags [kNumFlags], or null
 };
 
 hipError_t launch_cache_write(const CacheWriteParams& p, int src_kind,
@@ -99,6 +106,7 @@ struct CopyBlocksParams {
   int64_t block_bytes;    // bytes of one physical block (bs * Hkv * D * esize)
   int64_t src_blocks;     // pool sizes; pairs outside them are skipped
   int64_t dst_blocks;
+  int32_t* flags;         // caller's error flags [kNumFlags], or null
 };
 
 hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);

@@ -36,6 +36,7 @@ struct PrefillParams {
   // stride.  Workgroup (kv head, row tile, key piece) leaves one (max, sum,
   // unnormalised output) triple per row at slot pfx_slot0 + b * pfx_pieces
   // + piece of ws_acc [slots, Hq, D] / ws_ml [slots, Hq, 2].
+  int32_t* flags;         // caller's error flags [kNumFlags], or null
   float* ws_acc;
   float* ws_ml;
   int32_t pfx_slot0, pfx_pieces, pfx_tokens, pfx_chunk, pfx_row_tiles;

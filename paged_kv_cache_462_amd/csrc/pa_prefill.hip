@@ -175,6 +175,11 @@ void prefill_mfma_kernel(PrefillParams p) {
   // causal: rows of sequence b; prefix pass: all B * G (sequence, head) rows
   // device-resident sizes are clamped to what the buffers hold (a value
   // outside them is a caller error; clamping keeps every access in bounds)
+  if constexpr (!PFX) {
+    const int s0 = p.qsl[b], s1 = p.qsl[b + 1], len = p.lens[b];
+    if (s0 < 0 || s1 > p.T || s1 < s0) raise_flag(p.flags, kFlagQueryStart);
+    if (len < 0 || len > p.max_blocks * p.bs) raise_flag(p.flags, kFlagLength);
+  }
   const int q0 = PFX ? 0 : min(max(p.qsl[b], 0), p.T);
   const int n = PFX ? p.B * p.G : min(p.qsl[b + 1], p.T) - q0;
   const int L = PFX ? p.pfx_tokens : min(p.lens[b], p.max_blocks * p.bs);
@@ -273,7 +278,9 @@ void prefill_mfma_kernel(PrefillParams p) {
     auto fetch_ids = [&](int chunk) {
       const int tok0 = (chunk * 64 + lane) * 16;
       const int id = tok0 < kv_end ? tab[tok0 / p.bs] : 0;
-      return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
+      if ((unsigned)id < (unsigned)p.num_blocks) return id;
+      raise_flag(p.flags, kFlagBlockId);
+      return 0;
     };
     int ids_cur = fetch_ids(kt0 >> 4), ids_nxt = fetch_ids((kt0 >> 4) + 1), ids_chunk = kt0 >> 4;
 

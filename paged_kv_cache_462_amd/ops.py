@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import PaLaunch, PaTensor, check, load
+from ._lib import PA_NUM_FLAGS, PaLaunch, PaTensor, check, load
 
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 
@@ -52,8 +52,14 @@ def _desc(t: torch.Tensor, fp8: bool = False, scale: float = 1.0) -> PaTensor:
 
 def _launch(ref: torch.Tensor, workspace: Optional[torch.Tensor] = None,
             partition_tokens: int = 0, path: int = PATH_AUTO,
-            stream: Optional[torch.cuda.Stream] = None) -> PaLaunch:
+            stream: Optional[torch.cuda.Stream] = None,
+            error_flags: Optional[torch.Tensor] = None) -> PaLaunch:
     ln = PaLaunch()
+    if error_flags is not None:
+        if (error_flags.dtype != torch.int32 or error_flags.numel() < PA_NUM_FLAGS
+                or not error_flags.is_contiguous()):
+            raise ValueError(f"error_flags must be a contiguous int32 tensor of {PA_NUM_FLAGS}")
+        ln.error_flags = error_flags.data_ptr()
     if ref.is_cuda:
         s = stream if stream is not None else torch.cuda.current_stream(ref.device)
         ln.stream = s.cuda_stream
@@ -75,12 +81,13 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, slot_mapping: torc
                       key_cache: torch.Tensor, value_cache: torch.Tensor,
                       k_scale: float = 1.0, v_scale: float = 1.0,
                       kv_dtype: Optional[str] = None,
-                      stream: Optional[torch.cuda.Stream] = None) -> None:
+                      stream: Optional[torch.cuda.Stream] = None,
+                      error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_reshape_and_cache: key/value [T, Hkv, D] into slots of the caches."""
     fp8 = _is_fp8(key_cache, kv_dtype)
     args = (_desc(key), _desc(value), _desc(slot_mapping),
             _desc(key_cache, fp8, k_scale), _desc(value_cache, fp8, v_scale))
-    ln = _launch(key_cache, stream=stream)
+    ln = _launch(key_cache, stream=stream, error_flags=error_flags)
     check(load().pa_reshape_and_cache(*(byref(a) for a in args), byref(ln)))
 
 
@@ -110,7 +117,8 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
            scale: float, block_size: int, num_kv_heads: int,
            k_scale: float = 1.0, v_scale: float = 1.0, kv_dtype: Optional[str] = None,
            workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
-           path: int = PATH_AUTO, stream: Optional[torch.cuda.Stream] = None) -> None:
+           path: int = PATH_AUTO, stream: Optional[torch.cuda.Stream] = None,
+           error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_decode.  When the plan splits and no workspace is given, one is
     allocated here (torch owns it); pass `workspace` to avoid that."""
     fp8 = _is_fp8(key_cache, kv_dtype)
@@ -122,7 +130,7 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
             workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens))
-    ln = _launch(query, workspace, partition_tokens, path, stream)
+    ln = _launch(query, workspace, partition_tokens, path, stream, error_flags)
     check(load().pa_decode(*(byref(a) for a in args), ctypes.c_float(scale),
                            int(block_size), int(num_kv_heads), byref(ln)))
 
@@ -141,7 +149,8 @@ def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torc
                          k_scale: float = 1.0, v_scale: float = 1.0,
                          kv_dtype: Optional[str] = None,
                          workspace: Optional[torch.Tensor] = None,
-                         stream: Optional[torch.cuda.Stream] = None) -> None:
+                         stream: Optional[torch.cuda.Stream] = None,
+                         error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_decode_shared_prefix: decode of a batch whose sequences share their
     first prefix_tokens tokens (the blocks in prefix_blocks).  Without a
     workspace one is allocated here (torch owns it)."""
@@ -154,7 +163,7 @@ def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torc
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
             _desc(prefix_blocks))
-    ln = _launch(query, workspace, 0, PATH_AUTO, stream)
+    ln = _launch(query, workspace, 0, PATH_AUTO, stream, error_flags)
     check(load().pa_decode_shared_prefix(*(byref(a) for a in args), int(prefix_tokens),
                                          ctypes.c_float(scale), int(block_size),
                                          int(num_kv_heads), byref(ln)))
@@ -165,39 +174,42 @@ def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
             query_start_loc: torch.Tensor, max_query_len: int, scale: float, block_size: int,
             num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0,
             kv_dtype: Optional[str] = None,
-            stream: Optional[torch.cuda.Stream] = None) -> None:
+            stream: Optional[torch.cuda.Stream] = None,
+            error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_prefill: causal attention of the packed new rows of every sequence
     over its cached tokens (the new tokens' K/V already written)."""
     fp8 = _is_fp8(key_cache, kv_dtype)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
             _desc(query_start_loc))
-    ln = _launch(query, None, 0, PATH_AUTO, stream)
+    ln = _launch(query, None, 0, PATH_AUTO, stream, error_flags)
     check(load().pa_prefill(*(byref(a) for a in args), int(max_query_len),
                             ctypes.c_float(scale), int(block_size), int(num_kv_heads),
                             byref(ln)))
 
 
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,
-                kv_dtype: Optional[str] = None, stream: Optional[torch.cuda.Stream] = None) -> None:
+                kv_dtype: Optional[str] = None, stream: Optional[torch.cuda.Stream] = None,
+                error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_copy_blocks: key/value_cache[dst] = key/value_cache[src] per pair."""
     fp8 = _is_fp8(key_cache, kv_dtype)
     args = (_desc(key_cache, fp8, 1.0), _desc(value_cache, fp8, 1.0), _desc(block_pairs))
-    ln = _launch(key_cache, stream=stream)
+    ln = _launch(key_cache, stream=stream, error_flags=error_flags)
     check(load().pa_copy_blocks(*(byref(a) for a in args), byref(ln)))
 
 
 def swap_blocks(dst_key_cache: torch.Tensor, dst_value_cache: torch.Tensor,
                 src_key_cache: torch.Tensor, src_value_cache: torch.Tensor,
                 block_pairs: torch.Tensor, kv_dtype: Optional[str] = None,
-                stream: Optional[torch.cuda.Stream] = None) -> None:
+                stream: Optional[torch.cuda.Stream] = None,
+                error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_swap_blocks: dst_*[dst] = src_*[src] per (src, dst) pair; either
     pair of pools may be pinned host memory."""
     fp8 = _is_fp8(dst_key_cache, kv_dtype)
     args = (_desc(dst_key_cache, fp8, 1.0), _desc(dst_value_cache, fp8, 1.0),
             _desc(src_key_cache, fp8, 1.0), _desc(src_value_cache, fp8, 1.0), _desc(block_pairs))
     dev = dst_key_cache if dst_key_cache.is_cuda else src_key_cache
-    ln = _launch(dev, stream=stream)
+    ln = _launch(dev, stream=stream, error_flags=error_flags)
     check(load().pa_swap_blocks(*(byref(a) for a in args), byref(ln)))
 
 

@@ -99,14 +99,15 @@ def oracle_caches(wl: Workload):
 
 
 def gpu_decode(wl: Workload, d: Dev, partition_tokens: int = 0, path: int = 0,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               out: Optional[torch.Tensor] = None,
+               error_flags: Optional[torch.Tensor] = None) -> torch.Tensor:
     c = wl.cfg
     if out is None:
         out = torch.empty_like(d.query)
     pa.decode(out, d.query, d.kc, d.vc, d.tables, d.lens, wl.scale, c.block_size,
               c.num_kv_heads, k_scale=wl.k_scale, v_scale=wl.v_scale,
               kv_dtype="fp8" if c.kv_dtype == "fp8" else None,
-              partition_tokens=partition_tokens, path=path)
+              partition_tokens=partition_tokens, path=path, error_flags=error_flags)
     return out
 
 
@@ -117,17 +118,19 @@ def oracle_decode(wl: Workload, kc, vc, pairs: Optional[Sequence] = None) -> np.
 
 
 def gpu_prefill(wl: Workload, d: Dev, rows: PrefillRows, max_query_len: Optional[int] = None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, qsl: Optional[torch.Tensor] = None,
+                error_flags: Optional[torch.Tensor] = None) -> torch.Tensor:
     c = wl.cfg
     dev = d.kc.device
     q = rows.query.to(dev)
-    qsl = torch.from_numpy(rows.query_start_loc).to(dev)
+    if qsl is None:
+        qsl = torch.from_numpy(rows.query_start_loc).to(dev)
     if out is None:
         out = torch.empty_like(q)
     mq = rows.max_query_len if max_query_len is None else max_query_len
     pa.prefill(out, q, d.kc, d.vc, d.tables, d.lens, qsl, mq, wl.scale, c.block_size,
                c.num_kv_heads, k_scale=wl.k_scale, v_scale=wl.v_scale,
-               kv_dtype="fp8" if c.kv_dtype == "fp8" else None)
+               kv_dtype="fp8" if c.kv_dtype == "fp8" else None, error_flags=error_flags)
     return out
 
 

@@ -3,6 +3,7 @@
  * work, and a serving-style host flow -- allocator, block manager with a
  * shared prefix found by the prefix cache, fork and copy-on-write pairs,
  * exported block tables.  Exits non-zero on the first failed check. */
+#include <stddef.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -19,6 +20,15 @@ static int g_fail = 0;
 
 int main(void) {
   CHECK(strstr(pa_build_info(), "gfx950") != NULL);
+  /* struct layouts, for bindings in other languages */
+  printf("layout pa_tensor %zu %zu %zu %zu %zu %zu\n", sizeof(pa_tensor),
+         offsetof(pa_tensor, dtype), offsetof(pa_tensor, ndim), offsetof(pa_tensor, shape),
+         offsetof(pa_tensor, stride), offsetof(pa_tensor, scale));
+  printf("layout pa_launch %zu %zu %zu %zu %zu %zu\n", sizeof(pa_launch),
+         offsetof(pa_launch, workspace), offsetof(pa_launch, workspace_bytes),
+         offsetof(pa_launch, partition_tokens), offsetof(pa_launch, path),
+         offsetof(pa_launch, error_flags));
+  CHECK(PA_NUM_FLAGS == 4 && PA_FLAG_QUERY_START == 3);
 
   /* decode plan: 32 sequences, 32 heads, d 128, bs 16, up to 2048 tokens */
   pa_decode_plan_info info;

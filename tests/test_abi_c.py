@@ -1,6 +1,7 @@
 """The C ABI used from a plain C99 program (tests/native/abi_c.c): compiled
 with gcc against include/pa.h, linked to libpa.so, run on the CPU."""
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -25,3 +26,11 @@ def test_c_program_uses_the_abi(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stderr + r.stdout
     assert "abi ok" in r.stdout
+    # the ctypes binding lays the structs out as the C compiler does
+    lay = {ln.split()[1]: [int(x) for x in ln.split()[2:]]
+           for ln in r.stdout.splitlines() if ln.startswith("layout ")}
+    T, L = _lib.PaTensor, _lib.PaLaunch
+    assert lay["pa_tensor"] == [ctypes.sizeof(T), T.dtype.offset, T.ndim.offset, T.shape.offset,
+                                T.stride.offset, T.scale.offset]
+    assert lay["pa_launch"] == [ctypes.sizeof(L), L.workspace.offset, L.workspace_bytes.offset,
+                                L.partition_tokens.offset, L.path.offset, L.error_flags.offset]

@@ -4,7 +4,9 @@ block table reaches or negative, and cache-write slots outside the cache.
 The calls stay inside their buffers and give what the oracle gives on the
 contents taken the documented way: an id outside the pool reads block 0, a
 length is clamped to [0, max_blocks * block_size], an out-of-cache slot is
-skipped."""
+skipped.  A caller's error-flag array (the launch's error_flags) gets the
+flag of every kind of content taken that way, and no other; a clean call
+leaves it zero."""
 
 import numpy as np
 import pytest
@@ -18,6 +20,17 @@ from tests import _gpu as G
 pytestmark = pytest.mark.gpu
 
 VALU, MFMA = 1, 2
+BLOCK, LENGTH, SLOT, QSTART = (pa.PA_FLAG_BLOCK_ID, pa.PA_FLAG_LENGTH, pa.PA_FLAG_SLOT,
+                               pa.PA_FLAG_QUERY_START)
+
+
+def _flags():
+    return torch.zeros(pa.PA_NUM_FLAGS, dtype=torch.int32, device="cuda")
+
+
+def _raised(flags):
+    torch.cuda.synchronize()
+    return {k for k, v in enumerate(flags.tolist()) if v}
 LENS = [300, 200, 150, 90, 512, 60]  # 512: the whole table, so a clamped length reads real tokens
 
 CASES = {
@@ -67,9 +80,11 @@ def test_decode_with_bad_ids_and_lengths(name):
     paths = (VALU,) if wl.cfg.q_dtype == "f32" else (VALU, MFMA)
     for path in paths:
         for pt in (0, 512):
-            out = G.gpu_decode(wl, d, partition_tokens=pt, path=path)
+            flags = _flags()
+            out = G.gpu_decode(wl, d, partition_tokens=pt, path=path, error_flags=flags)
             torch.cuda.synchronize()
             G.assert_close(out, ref, atol, rtol, what=f"untrusted decode {name} path={path} pt={pt}")
+            assert _raised(flags) == {BLOCK, LENGTH}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -79,10 +94,12 @@ def test_prefill_with_bad_ids_and_lengths(name):
     G.say(f"untrusted prefill {name}")
     ref = G.oracle_prefill(clean, kc, vc, rows)
     assert not np.isnan(ref).any()
-    out = G.gpu_prefill(wl, d, rows)
+    flags = _flags()
+    out = G.gpu_prefill(wl, d, rows, error_flags=flags)
     torch.cuda.synchronize()
     atol, rtol = G.tol_for(wl)
     G.assert_close(out, ref, atol, rtol, what=f"untrusted prefill {name}")
+    assert _raised(flags) == {BLOCK, LENGTH}
 
 
 @pytest.mark.parametrize("name", ["bf16_g8", "fp8_g4"])
@@ -99,10 +116,66 @@ def test_cache_write_skips_slots_outside_the_cache(name):
     clean[bad] = -1
     d = G.to_device(wl, fill=False)
     kvd = "fp8" if wl.cfg.kv_dtype == "fp8" else None
+    flags = _flags()
     pa.reshape_and_cache(d.tok_key, d.tok_value, torch.from_numpy(slots).to(d.kc.device), d.kc, d.vc,
-                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
-    torch.cuda.synchronize()
+                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, error_flags=flags)
+    assert _raised(flags) == {SLOT}
     wl2 = type(wl)(**{**wl.__dict__})
     wl2.slot_mapping = clean
     kc, vc = G.oracle_caches(wl2)
     assert G.caches_equal(d.kc, kc) and G.caches_equal(d.vc, vc)
+
+
+@pytest.mark.parametrize("name", ["bf16_g8", "fp8_g4"])
+def test_clean_calls_raise_no_flag(name):
+    """Valid contents (negative cache-write slots included, which skip by
+    contract): every call leaves the flags at zero."""
+    wl = make_workload(CASES[name], seed=95)
+    G.say(f"clean flags {name}")
+    d = G.to_device(wl, fill=False)
+    kvd = "fp8" if wl.cfg.kv_dtype == "fp8" else None
+    slots = wl.slot_mapping.copy()
+    slots[7] = -1
+    flags = _flags()
+    pa.reshape_and_cache(d.tok_key, d.tok_value, torch.from_numpy(slots).to(d.kc.device), d.kc, d.vc,
+                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd, error_flags=flags)
+    for path in (VALU, MFMA):
+        for pt in (0, -1, 64):
+            G.gpu_decode(wl, d, partition_tokens=pt, path=path, error_flags=flags)
+    rows = make_prefill_rows(wl, ("list", [100, 200, 150, 1, 250, 60]), seed=96)
+    G.gpu_prefill(wl, d, rows, error_flags=flags)
+    pairs = torch.tensor([[int(wl.block_tables[0, 0]), 0]], dtype=torch.int32, device="cuda")
+    pa.copy_blocks(d.kc, d.vc, pairs, kv_dtype=kvd, error_flags=flags)
+    assert _raised(flags) == set()
+
+
+def test_prefill_flags_query_start_past_the_rows():
+    """query_start_loc ending past the packed rows is clamped to them (the
+    same rows as the clean call) and raises the query-start flag."""
+    wl = make_workload(CASES["bf16_g8"], seed=97)
+    rows = make_prefill_rows(wl, ("list", [100, 200, 150, 1, 250, 60]), seed=98)
+    G.say("untrusted query_start_loc")
+    d = G.to_device(wl)
+    clean = G.gpu_prefill(wl, d, rows)
+    qsl = rows.query_start_loc.copy()
+    qsl[-1] += 5
+    flags = _flags()
+    out = G.gpu_prefill(wl, d, rows, qsl=torch.from_numpy(qsl).to(d.kc.device), error_flags=flags)
+    assert _raised(flags) == {QSTART}
+    assert torch.equal(out, clean)
+
+
+def test_copy_blocks_flags_pairs_outside_the_pool():
+    """A block pair naming a block outside the pool is skipped and raises the
+    block-id flag; the valid pair of the same call is copied."""
+    G.say("untrusted block copy")
+    shape = (12, 16, 2, 128)
+    kc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.randn(shape, dtype=torch.bfloat16, device="cuda")
+    k0, v0 = kc.clone(), vc.clone()
+    pairs = torch.tensor([[1, 2], [3, 12], [-1, 4]], dtype=torch.int32, device="cuda")
+    flags = _flags()
+    pa.copy_blocks(kc, vc, pairs, error_flags=flags)
+    assert _raised(flags) == {BLOCK}
+    k0[2], v0[2] = k0[1], v0[1]
+    assert torch.equal(kc, k0) and torch.equal(vc, v0)
