@@ -49,7 +49,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from .attention import gather_tokens, kv_head_for
+from .attention import gather_tokens
 
 
 def row_positions(n: int, L: int) -> np.ndarray:

@@ -7,7 +7,7 @@ inside a block, exactly on a block boundary, and at zero."""
 import pytest
 import torch
 
-from synth import get_config, get_prefill_config, make_prefill_rows, make_workload
+from synth import get_config, make_prefill_rows, make_workload
 from synth.generate import shrink
 from tests import _gpu as G
 

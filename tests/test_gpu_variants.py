@@ -9,7 +9,6 @@ than a 512-token partition) and each under the three schedules: balanced
 
 import itertools
 
-import numpy as np
 import pytest
 import torch
 

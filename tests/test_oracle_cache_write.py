@@ -5,7 +5,6 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention as A
 from oracle import cache_write as W
 from oracle import fp8
 from synth import get_config, make_workload

@@ -2,7 +2,6 @@
 constants of the OCP E4M3FN format."""
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import fp8
