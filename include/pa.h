@@ -203,10 +203,20 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
  *   scale           score scale, positive and finite (1/sqrt(D) for standard
  *                   attention)
  *   block_size (a multiple of 16), num_kv_heads: as for pa_decode
- *   launch          stream (workspace and partitioning unused); NULL = null
- *                   stream
- * Supported head_dim: 64, 128.  No workspace; deterministic.  Asynchronous on
- * launch->stream.
+ *   launch          stream; NULL = null stream.  Partitioning unused.  The
+ *                   workspace is optional and only used for a bf16 query
+ *                   with bf16 K/V: given pa_prefill_workspace_bytes(...)
+ *                   bytes (4-byte aligned, caller-owned, any contents), the
+ *                   P x V product runs in f16 (V converted exactly, which
+ *                   holds for |v| < 2^16; smaller than 2^-14 rounds to f16's
+ *                   subnormal spacing, an absolute error below 2^-25) and
+ *                   a second launch recomputes, with the bf16 product, every
+ *                   workgroup that met a wider V value; without it (or
+ *                   smaller) the bf16 product runs throughout, P as a high
+ *                   and a low bf16 part with a product each.  A bf16 query
+ *                   with fp8 K/V always runs P x V in f16 (its values fit).
+ * Supported head_dim: 64, 128.  Deterministic.  Asynchronous on
+ * launch->stream; calls that share a workspace must not overlap.
  */
 int pa_prefill(pa_tensor* out, const pa_tensor* query,
                const pa_tensor* key_cache, const pa_tensor* value_cache,
@@ -214,6 +224,14 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query,
                const pa_tensor* query_start_loc, int32_t max_query_len,
                float scale, int32_t block_size, int32_t num_kv_heads,
                const pa_launch* launch);
+
+/*
+ * Workspace bytes that let pa_prefill run a bf16 query's P x V product in
+ * f16 (one int32 per workgroup of its grid): batch = B, num_rows = T and
+ * max_query_len as passed to pa_prefill.  Negative status on negative sizes.
+ */
+int64_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_rows,
+                                   int32_t max_query_len);
 
 /*
  * pa_decode_shared_prefix -- pa_decode for a batch whose sequences all start

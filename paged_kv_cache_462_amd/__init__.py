@@ -32,6 +32,7 @@ from .ops import (  # noqa: F401
     decode_shared_prefix_workspace_bytes,
     decode_workspace_bytes,
     prefill,
+    prefill_workspace_bytes,
     reshape_and_cache,
     swap_blocks,
 )

@@ -70,6 +70,7 @@ SIGNATURES = {
     "pa_copy_blocks": (c_int32, [_T, _T, _T, _L]),
     "pa_swap_blocks": (c_int32, [_T, _T, _T, _T, _T, _L]),
     "pa_decode_workspace_bytes": (c_int64, [c_int32] * 7),
+    "pa_prefill_workspace_bytes": (c_int64, [c_int32] * 4),
     "pa_decode_plan": (c_int32, [c_int32] * 7 + [POINTER(PaDecodePlan)]),
     "pa_last_error": (c_char_p, []),
     "pa_build_info": (c_char_p, []),

@@ -105,6 +105,18 @@ struct Plan {
 // reads seq_lens (they live on the device): the balanced schedule finds the
 // lengths on the device, and a fixed split covers the table width (its
 // partitions past a sequence's end exit at once).
+// Query-tile ranks of the prefill grid (Hq * ranks * B workgroups; past
+// 2^24 workgroups the kernel loops over the remaining ranks instead).
+int64_t prefill_ranks(int64_t B, int64_t Hq, int64_t T, int64_t max_query_len) {
+  const int64_t bm = pa::prefill_rows_per_workgroup();
+  const int64_t mq = max_query_len > 0 && max_query_len < T ? max_query_len : T;
+  int64_t ranks = (mq + bm - 1) / bm;
+  const int64_t per_rank = Hq * B;
+  if (per_rank > 0 && ranks * per_rank > (1LL << 24))
+    ranks = (1LL << 24) / per_rank > 0 ? (1LL << 24) / per_rank : 1;
+  return ranks;
+}
+
 // The caller's error flags (launch->error_flags): null, or 4-byte aligned.
 int flags_of(const pa_launch* launch, int32_t** out) {
   *out = launch ? launch->error_flags : nullptr;
@@ -586,12 +598,7 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
     return fail(PA_ERR_UNSUPPORTED, "no prefill variant for this dtype / head_dim (64 and 128 are built)");
   if (B == 0 || T == 0 || Hq == 0) return PA_OK;
 
-  const int64_t bm = pa::prefill_rows_per_workgroup();
-  const int64_t mq = max_query_len > 0 && max_query_len < T ? max_query_len : T;
-  int64_t ranks = (mq + bm - 1) / bm;
-  // grid = Hq * ranks * B workgroups; past 2^24 the kernel loops instead
-  const int64_t per_rank = Hq * B;
-  if (ranks * per_rank > (1LL << 24)) ranks = (1LL << 24) / per_rank > 0 ? (1LL << 24) / per_rank : 1;
+  const int64_t ranks = prefill_ranks(B, Hq, T, max_query_len);
   pa::PrefillParams p;
   memset(&p, 0, sizeof p);
   int frc = flags_of(launch, &p.flags);
@@ -625,10 +632,26 @@ int pa_prefill(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cach
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
+  // bf16 query and K/V: with a workspace for the per-workgroup flags, P x V
+  // runs in f16 (and a second launch redoes the flagged workgroups in bf16)
+  if (qdt == PA_BF16 && kvdt == PA_BF16 && launch && launch->workspace) {
+    const int64_t need = pa::prefill_grid_size(B, Hq, ranks) * (int64_t)sizeof(int32_t);
+    if (reinterpret_cast<uintptr_t>(launch->workspace) % 4)
+      return fail(PA_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+    if (launch->workspace_bytes >= (size_t)need) p.wide_flags = static_cast<int32_t*>(launch->workspace);
+  }
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
   hipError_t e = pa::launch_prefill(p, kind_of(qdt), kind_of(kvdt), stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+int64_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_rows,
+                                   int32_t max_query_len) {
+  if (batch < 0 || num_q_heads < 0 || num_rows < 0)
+    return fail(PA_ERR_INVALID_ARG, "sizes must not be negative");
+  const int64_t ranks = prefill_ranks(batch, num_q_heads, num_rows, max_query_len);
+  return pa::prefill_grid_size(batch, num_q_heads, ranks) * (int64_t)sizeof(int32_t);
 }
 
 namespace {

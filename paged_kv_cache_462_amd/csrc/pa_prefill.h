@@ -36,17 +36,28 @@ struct PrefillParams {
   // stride.  Workgroup (kv head, row tile, key piece) leaves one (max, sum,
   // unnormalised output) triple per row at slot pfx_slot0 + b * pfx_pieces
   // + piece of ws_acc [slots, Hq, D] / ws_ml [slots, Hq, 2].
-  int32_t* flags;         // caller's error flags [kNumFlags], or null
   float* ws_acc;
   float* ws_ml;
   int32_t pfx_slot0, pfx_pieces, pfx_tokens, pfx_chunk, pfx_row_tiles;
+  int32_t* flags;         // caller's error flags [kNumFlags], or null
+  // bf16 query and bf16 K/V (causal prefill): one int per workgroup of the
+  // grid, or null.  With it the prefill runs P x V in f16 (V converted while
+  // staged, exact below 2^16) and each workgroup stores whether it met a V
+  // value outside f16's range; a second launch recomputes exactly those
+  // workgroups with the bf16 product (the others exit at once).
+  int32_t* wide_flags;
 };
 
 // Query rows one workgroup takes.
 int prefill_rows_per_workgroup();
 
 // hipErrorNotSupported when no built variant matches (qkind, kvkind, D).
+// A bf16 query with fp8 K/V runs P x V in f16 (fp8 values always fit); with
+// bf16 K/V it does when p.wide_flags is set (two launches), else in bf16.
 hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream);
+
+// Workgroups of the causal prefill grid (the wide_flags entries it needs).
+int64_t prefill_grid_size(int64_t B, int64_t Hq, int64_t tile_ranks);
 
 bool prefill_variant_built(int qkind, int kvkind, int D);
 

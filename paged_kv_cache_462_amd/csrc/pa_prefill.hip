@@ -46,9 +46,14 @@
 //    movement, and the V^T operand comes straight out of LDS transpose
 //    reads (ds_read_b64_tr_b16); a row of ones as V^T gives the weight sums
 //    on the matrix cores as well;
-//  * bf16 P is split into a high and a low bf16 part, each with its own
-//    product, so that the weights keep ~16 significant bits (a single bf16
-//    P uses most of the error budget of a 16-bit result).
+//  * P needs more than bf16's 8 significant bits (a single bf16 P uses most
+//    of the error budget of a 16-bit result).  A bf16 query therefore runs
+//    P x V in f16 with f16 P (11 bits, like the f16 query): V is converted
+//    to f16 while staged (fp8 V decodes to f16 directly), exactly for bf16
+//    values below 2^16.  A workgroup that staged a wider value is flagged
+//    and recomputed by a second launch in bf16, P split into a high and a
+//    low bf16 part with a product each (~16 significant bits).  Without
+//    the flag array the bf16 product runs throughout.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -76,6 +81,11 @@ constexpr int kBM = kWaves * kQSub * 16;     // query rows per workgroup
 // largest growth of a row max (log2 units) absorbed without rescaling the
 // accumulated output: weights stay below 2^8, far inside f16 / bf16 range
 constexpr float kLazyRescale = 8.0f;
+// bf16 magnitude bits (sign cleared) from which a value no longer fits f16:
+// 0x4780 is 2^16, and everything above it up to inf and NaN.  Below it a
+// bf16 value converts to f16 exactly down to 2^-14; smaller ones round to
+// f16's subnormal spacing (2^-24), an absolute error below 2^-25.
+constexpr uint32_t kBf16F16Limit = 0x4780u;
 
 template <int KIND>
 struct Esz {
@@ -107,7 +117,7 @@ __device__ __forceinline__ i32x2 lds_tr16(const char* p) {
 // decode batch (see PrefillParams): the same tile machinery with rows taken
 // from every sequence, a per-row key limit instead of the causal one, one
 // key piece per workgroup, and triples instead of normalised rows.
-template <int QK, int KVK, int D, bool PFX>
+template <int QK, int KVK, int D, bool PFX, bool F16PV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_EU)))
 void prefill_mfma_kernel(PrefillParams p) {
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
@@ -126,7 +136,14 @@ void prefill_mfma_kernel(PrefillParams p) {
   constexpr int kStagePasses = kBN / kStageRows;
   constexpr int KS = D / 32;    // k-steps of the score product
   constexpr int ESZ = Esz<KVK>::v;
-  constexpr int kOne2 = BF ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
+  // F16PV (bf16 query only): V is staged as f16 (fp8 V decodes to f16;
+  // bf16 V converts exactly below 2^16) and P x V runs in f16 with f16 P,
+  // one product.  Otherwise P x V runs in the query's type, bf16 P as a hi
+  // and a lo part with a product each.
+  constexpr bool BFPV = BF && !F16PV;
+  constexpr bool kCheckWide = F16PV && KVK == K_BF16;
+  static_assert(!F16PV || (BF && !PFX), "f16 P x V is a bf16-query prefill variant");
+  constexpr int kOne2 = BFPV ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
   const i32x4 kOnes = i32x4{kOne2, kOne2, kOne2, kOne2};
   // K and V tiles, double-buffered, with the padded pitches above: the
   // operand reads below are conflict-free with plain (immediate-offset)
@@ -134,6 +151,10 @@ void prefill_mfma_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) char k_lds[2][kBN * kRowK];
   __shared__ __attribute__((aligned(16))) char v_lds[2][kBN * kRowV];
 
+  if constexpr (!PFX && BFPV && KVK == K_BF16) {
+    // second launch after the f16 pass: only the workgroups it flagged
+    if (p.wide_flags && p.wide_flags[blockIdx.x] == 0) return;
+  }
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
@@ -209,6 +230,7 @@ void prefill_mfma_kernel(PrefillParams p) {
 
   // causal: heaviest tile first, looping when the grid has fewer ranks than
   // tiles; prefix pass: exactly row tile `rank`
+  bool wide = false;  // f16 pass: a staged V value outside f16's range
   for (int tile = PFX ? rank : ntiles - 1 - rank; tile >= 0; tile = PFX ? -1 : tile - p.tile_ranks) {
     const int row0 = tile * kBM;
     const int rows = min(kBM, n - row0);
@@ -302,7 +324,7 @@ void prefill_mfma_kernel(PrefillParams p) {
           const int in_blk = p.spb_shift >= 0 ? (sub & ((1 << p.spb_shift) - 1)) * 16 : sub0 % p.bs;
           const int64_t ub = (int64_t)blk * blk_bytes + (int64_t)in_blk * tok_bytes;
           kr[i] = load_chunk<KVK, BF>(kbase + ub + lane_off);
-          vr[i] = load_chunk<KVK, BF>(vbase + ub + lane_off);
+          vr[i] = load_chunk<KVK, BFPV>(vbase + ub + lane_off);
         } else {
           kr[i] = i32x4{0, 0, 0, 0};
           vr[i] = i32x4{0, 0, 0, 0};
@@ -315,12 +337,28 @@ void prefill_mfma_kernel(PrefillParams p) {
     for (int kt = kt0; kt < ntk; ++kt) {
       const int buf = kt & 1;
       const int key0 = kt * kBN;
+      // bf16 V on the f16 path: converted here; `wide` notes a value
+      // outside f16's range
+      auto v_stage = [&](const i32x4& raw) {
+        if constexpr (kCheckWide) {
+          i32x4 o2;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w2 = (uint32_t)raw[e];
+            wide |= (w2 & 0x7FFFu) >= kBf16F16Limit || (w2 >> 16 & 0x7FFFu) >= kBf16F16Limit;
+            o2[e] = (int)pack_f16(bf16_lo(w2), bf16_hi(w2));
+          }
+          return o2;
+        } else {
+          return raw;
+        }
+      };
       if (key0 + kBN <= kv_end) {
 #pragma unroll
         for (int i = 0; i < kStagePasses; ++i) {
           const int r = srow + kStageRows * i;
           *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowK + sch * 16]) = kr[i];
-          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) = vr[i];
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) = v_stage(vr[i]);
         }
       } else {
         // the keys end inside this tile: slots past the sequence's end hold
@@ -331,7 +369,8 @@ void prefill_mfma_kernel(PrefillParams p) {
           const int r = srow + kStageRows * i;
           const bool live = key0 + r < kv_end;
           *reinterpret_cast<i32x4*>(&k_lds[buf][r * kRowK + sch * 16]) = live ? kr[i] : i32x4{0, 0, 0, 0};
-          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) = live ? vr[i] : i32x4{0, 0, 0, 0};
+          *reinterpret_cast<i32x4*>(&v_lds[buf][r * kRowV + sch * 16]) =
+              v_stage(live ? vr[i] : i32x4{0, 0, 0, 0});
         }
       }
       __syncthreads();
@@ -400,7 +439,7 @@ void prefill_mfma_kernel(PrefillParams p) {
           for (int s2 = 0; s2 < 2; ++s2) {
             const float* a = x[2 * s2];
             const float* c = x[2 * s2 + 1];
-            if constexpr (BF) {
+            if constexpr (BFPV) {
               const uint32_t h0 = pack_bf16(a[0], a[1]), h1 = pack_bf16(a[2], a[3]);
               const uint32_t h2 = pack_bf16(c[0], c[1]), h3 = pack_bf16(c[2], c[3]);
               ph[qs][s2] = i32x4{(int)h0, (int)h1, (int)h2, (int)h3};
@@ -437,8 +476,8 @@ void prefill_mfma_kernel(PrefillParams p) {
           const i32x4 a = i32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
           for (int qs = 0; qs < kQSub; ++qs) {
-            o[qs][jb] = mfma_k32<BF>(a, ph[qs][s2], o[qs][jb]);
-            if constexpr (BF) o[qs][jb] = mfma_k32<BF>(a, pl[qs][s2], o[qs][jb]);
+            o[qs][jb] = mfma_k32<BFPV>(a, ph[qs][s2], o[qs][jb]);
+            if constexpr (BFPV) o[qs][jb] = mfma_k32<BFPV>(a, pl[qs][s2], o[qs][jb]);
           }
         }
         // the weight sums on the matrix cores too: a row of ones as V^T
@@ -446,8 +485,8 @@ void prefill_mfma_kernel(PrefillParams p) {
         // took (cheaper than 32 adds and two cross-lane steps per tile)
 #pragma unroll
         for (int qs = 0; qs < kQSub; ++qs) {
-          ls[qs] = mfma_k32<BF>(kOnes, ph[qs][s2], ls[qs]);
-          if constexpr (BF) ls[qs] = mfma_k32<BF>(kOnes, pl[qs][s2], ls[qs]);
+          ls[qs] = mfma_k32<BFPV>(kOnes, ph[qs][s2], ls[qs]);
+          if constexpr (BFPV) ls[qs] = mfma_k32<BFPV>(kOnes, pl[qs][s2], ls[qs]);
         }
       }
     }
@@ -490,13 +529,21 @@ void prefill_mfma_kernel(PrefillParams p) {
       }
     }
   }
+  if constexpr (kCheckWide) {
+    // every thread of the workgroup gets here: one flag per workgroup, 1
+    // when any of its tiles staged a V value outside f16's range
+    if (p.wide_flags) {
+      const int any = __syncthreads_or(wide ? 1 : 0);
+      if (threadIdx.x == 0) p.wide_flags[blockIdx.x] = any != 0;
+    }
+  }
 }
 
-template <int QK, int KVK, int D, bool PFX>
+template <int QK, int KVK, int D, bool PFX, bool F16PV = false>
 hipError_t launch_one(const PrefillParams& p, hipStream_t stream) {
   const dim3 grid(PFX ? (unsigned)(p.Hkv * p.pfx_row_tiles * p.pfx_pieces)
                       : (unsigned)(p.Hq * p.tile_ranks * p.B));
-  hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D, PFX>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((prefill_mfma_kernel<QK, KVK, D, PFX, F16PV>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -514,6 +561,16 @@ hipError_t launch_mode(const PrefillParams& p, int qkind, int kvkind, hipStream_
   return fp8 ? launch_one<K_BF16, K_FP8, 128, PFX>(p, stream) : launch_one<K_BF16, K_BF16, 128, PFX>(p, stream);
 }
 
+// bf16 query, P x V in f16: fp8 K/V in one launch; bf16 K/V in the f16
+// launch and the launch that redoes the flagged workgroups in bf16
+template <int D>
+hipError_t launch_bf16_f16pv(const PrefillParams& p, int kvkind, hipStream_t stream) {
+  if (kvkind == K_FP8) return launch_one<K_BF16, K_FP8, D, false, true>(p, stream);
+  const hipError_t e = launch_one<K_BF16, K_BF16, D, false, true>(p, stream);
+  if (e != hipSuccess) return e;
+  return launch_one<K_BF16, K_BF16, D, false, false>(p, stream);
+}
+
 }  // namespace
 
 int prefill_rows_per_workgroup() { return kBM; }
@@ -525,8 +582,15 @@ bool prefill_variant_built(int qkind, int kvkind, int D) {
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
-  return launch_mode<false>(p, qkind, kvkind, stream);
+  if (prefill_variant_built(qkind, kvkind, p.D) && qkind == K_BF16 &&
+      (kvkind == K_FP8 || p.wide_flags))
+    return p.D == 64 ? launch_bf16_f16pv<64>(p, kvkind, stream) : launch_bf16_f16pv<128>(p, kvkind, stream);
+  PrefillParams q = p;
+  q.wide_flags = nullptr;  // the plain bf16 launch redoes nothing
+  return launch_mode<false>(q, qkind, kvkind, stream);
 }
+
+int64_t prefill_grid_size(int64_t B, int64_t Hq, int64_t tile_ranks) { return Hq * tile_ranks * B; }
 
 hipError_t launch_prefix_pass(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
   return launch_mode<true>(p, qkind, kvkind, stream);

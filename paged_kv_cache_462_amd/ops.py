@@ -175,17 +175,30 @@ def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
             num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0,
             kv_dtype: Optional[str] = None,
             stream: Optional[torch.cuda.Stream] = None,
-            error_flags: Optional[torch.Tensor] = None) -> None:
+            error_flags: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> None:
     """pa_prefill: causal attention of the packed new rows of every sequence
-    over its cached tokens (the new tokens' K/V already written)."""
+    over its cached tokens (the new tokens' K/V already written).  A bf16
+    query with bf16 K/V takes the library's workspace for its f16 P x V
+    path; without one it is allocated here (torch owns it), and an empty
+    tensor runs the bf16 product instead."""
     fp8 = _is_fp8(key_cache, kv_dtype)
+    if workspace is None and query.dtype == torch.bfloat16 and key_cache.dtype == torch.bfloat16:
+        need = prefill_workspace_bytes(seq_lens.shape[0], query.shape[1], query.shape[0],
+                                       max_query_len)
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=query.device)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
             _desc(query_start_loc))
-    ln = _launch(query, None, 0, PATH_AUTO, stream, error_flags)
+    ln = _launch(query, workspace, 0, PATH_AUTO, stream, error_flags)
     check(load().pa_prefill(*(byref(a) for a in args), int(max_query_len),
                             ctypes.c_float(scale), int(block_size), int(num_kv_heads),
                             byref(ln)))
+
+
+def prefill_workspace_bytes(batch: int, num_q_heads: int, num_rows: int,
+                            max_query_len: int) -> int:
+    return check(load().pa_prefill_workspace_bytes(batch, num_q_heads, num_rows, max_query_len))
 
 
 def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, block_pairs: torch.Tensor,

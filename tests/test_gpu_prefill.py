@@ -179,3 +179,78 @@ def test_prefill_full_size(name):
     ref = G.oracle_prefill(wl, kc, vc, rows, subset)
     atol, rtol = G.tol_for(wl)
     G.assert_close(got[subset], ref[subset], atol, rtol, what=f"prefill full {name}")
+
+
+# --- bf16 query and K/V: the f16 P x V path and its bf16 redo ------------------
+
+def _bf16_case(seed, wide_tokens=()):
+    """The GQA bf16 small case, with the value rows of the given stream
+    tokens (at most one per sequence) set to magnitudes f16 cannot hold,
+    one sign per row, so their workgroups are redone with the bf16 product.
+    One sign per row and one such token per sequence: no output is the
+    near-cancellation of two huge terms, which no 16-bit weight resolves."""
+    base, lens, news = SMALL["gqa_bf16"]
+    cfg = shrink(base, batch=len(lens), lengths=("list", lens), pool_blocks=0)
+    wl = make_workload(cfg, seed=seed)
+    if wide_tokens:
+        v = wl.tok_value.float().clone()
+        for i, (t, mag) in enumerate(wide_tokens):
+            v[t] = mag * (1.0 + 0.01 * v[t])
+        wl = type(wl)(**{**wl.__dict__, "tok_value": v.to(torch.bfloat16)})
+    rows = make_prefill_rows(wl, news, seed=seed + 1)
+    return wl, rows
+
+
+def _ws(wl, rows):
+    need = pa.prefill_workspace_bytes(wl.cfg.batch, wl.cfg.num_q_heads, rows.num_rows,
+                                      rows.max_query_len)
+    assert need > 0 and need % 4 == 0
+    return torch.full((need // 4,), -1, dtype=torch.int32, device="cuda")
+
+
+def test_prefill_bf16_f16_path_and_plain_path():
+    """With the workspace (f16 P x V) and without it (bf16 hi + lo
+    products): both within tolerance of the oracle, no workgroup flagged on
+    N(0, 1) values."""
+    wl, rows = _bf16_case(201)
+    G.say("prefill bf16: f16 path vs bf16 path")
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_prefill(wl, kc, vc, rows)
+    d = G.to_device(wl)
+    ws = _ws(wl, rows)
+    c = wl.cfg
+    q = rows.query.to("cuda")
+    qsl = torch.from_numpy(rows.query_start_loc).to("cuda")
+    atol, rtol = G.tol_for(wl)
+    for what, w in (("f16 path", ws), ("bf16 path", torch.empty(0, dtype=torch.int32, device="cuda"))):
+        out = torch.empty_like(q)
+        pa.prefill(out, q, d.kc, d.vc, d.tables, d.lens, qsl, rows.max_query_len, wl.scale,
+                   c.block_size, c.num_kv_heads, workspace=w)
+        torch.cuda.synchronize()
+        G.assert_close(out, ref, atol, rtol, what=f"prefill bf16 {what}")
+    assert int(ws.max()) == 0 and int(ws.min()) == 0   # every workgroup wrote 0
+
+
+def test_prefill_bf16_wide_values_are_redone():
+    """Value rows of 7e4 .. 1e6 (beyond f16) in a few tokens: their
+    workgroups are flagged and recomputed with the bf16 product, the others
+    keep the f16 result; the whole output matches the oracle."""
+    # stream tokens: sequence 0 holds 0..999, sequence 1 1000..1256, 4 1264..
+    wl, rows = _bf16_case(203, wide_tokens=((700, 7.0e4), (1100, -3.0e5), (1300, 1.0e6)))
+    G.say("prefill bf16: wide values")
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_prefill(wl, kc, vc, rows)
+    assert np.isfinite(ref).all()
+    d = G.to_device(wl)
+    ws = _ws(wl, rows)
+    c = wl.cfg
+    q = rows.query.to("cuda")
+    qsl = torch.from_numpy(rows.query_start_loc).to("cuda")
+    out = torch.empty_like(q)
+    pa.prefill(out, q, d.kc, d.vc, d.tables, d.lens, qsl, rows.max_query_len, wl.scale,
+               c.block_size, c.num_kv_heads, workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws.cpu().numpy()
+    assert set(np.unique(flags)) == {0, 1}, np.unique(flags)   # some flagged, some not
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(out, ref, atol, rtol, what="prefill bf16 wide values")

@@ -460,3 +460,15 @@ def test_allocator_thread_hammer():
     assert not errors
     assert a.num_free() == 256
     assert all(a.refcount(b) == 0 for b in range(256))
+
+
+def test_prefill_workspace_bytes():
+    """One int32 per workgroup of the prefill grid: query heads x query-tile
+    ranks (256 rows each, from max_query_len, else the row count) x batch."""
+    lib = _lib.load()
+    assert lib.pa_prefill_workspace_bytes(8, 32, 16384, 2048) == 4 * 32 * 8 * 8
+    assert lib.pa_prefill_workspace_bytes(4, 64, 4096, 1024) == 4 * 64 * 4 * 4
+    assert lib.pa_prefill_workspace_bytes(4, 64, 4096, 0) == 4 * 64 * 16 * 4     # <= 0: the row count
+    assert lib.pa_prefill_workspace_bytes(3, 8, 300, 257) == 4 * 8 * 2 * 3
+    assert lib.pa_prefill_workspace_bytes(0, 8, 0, 0) == 0
+    assert lib.pa_prefill_workspace_bytes(-1, 8, 10, 10) == _lib.PA_ERR_INVALID_ARG
