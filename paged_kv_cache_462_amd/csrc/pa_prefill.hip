@@ -142,7 +142,8 @@ void prefill_mfma_kernel(PrefillParams p) {
   // and a lo part with a product each.
   constexpr bool BFPV = BF && !F16PV;
   constexpr bool kCheckWide = F16PV && KVK == K_BF16;
-  static_assert(!F16PV || (BF && !PFX), "f16 P x V is a bf16-query prefill variant");
+  static_assert(!F16PV || (BF && (!PFX || KVK == K_FP8)),
+                "f16 P x V: bf16 query; in the prefix pass only with fp8 K/V (no flags)");
   constexpr int kOne2 = BFPV ? 0x3F803F80 : 0x3C003C00;  // two 16-bit ones
   const i32x4 kOnes = i32x4{kOne2, kOne2, kOne2, kOne2};
   // K and V tiles, double-buffered, with the padded pitches above: the
@@ -593,6 +594,10 @@ hipError_t launch_prefill(const PrefillParams& p, int qkind, int kvkind, hipStre
 int64_t prefill_grid_size(int64_t B, int64_t Hq, int64_t tile_ranks) { return Hq * tile_ranks * B; }
 
 hipError_t launch_prefix_pass(const PrefillParams& p, int qkind, int kvkind, hipStream_t stream) {
+  // fp8 values always fit f16: a bf16 query takes the f16 product there
+  if (prefill_variant_built(qkind, kvkind, p.D) && qkind == K_BF16 && kvkind == K_FP8)
+    return p.D == 64 ? launch_one<K_BF16, K_FP8, 64, true, true>(p, stream)
+                     : launch_one<K_BF16, K_FP8, 128, true, true>(p, stream);
   return launch_mode<true>(p, qkind, kvkind, stream);
 }
 
