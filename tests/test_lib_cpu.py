@@ -472,3 +472,24 @@ def test_prefill_workspace_bytes():
     assert lib.pa_prefill_workspace_bytes(3, 8, 300, 257) == 4 * 8 * 2 * 3
     assert lib.pa_prefill_workspace_bytes(0, 8, 0, 0) == 0
     assert lib.pa_prefill_workspace_bytes(-1, 8, 10, 10) == _lib.PA_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_misaligned_workspace_and_flags():
+    """Checked on the host, before any launch: a bf16 prefill's workspace
+    (its f16-product flags) and any call's error flags must be 4-byte
+    aligned."""
+    a = _prefill_args()
+    lib = _lib.load()
+
+    def call(ln):
+        return lib.pa_prefill(
+            ctypes.byref(a["out"]), ctypes.byref(a["query"]), ctypes.byref(a["kc"]),
+            ctypes.byref(a["vc"]), ctypes.byref(a["tab"]), ctypes.byref(a["lens"]),
+            ctypes.byref(a["qsl"]), a["mq"], 0.1, a["bs"], a["hkv"], ctypes.byref(ln))
+
+    _expect(call(PaLaunch(None, FAKE + 2, 1 << 20, 0, 0)), _lib.PA_ERR_INVALID_ARG)
+    _expect(call(PaLaunch(None, None, 0, 0, 0, FAKE + 2)), _lib.PA_ERR_INVALID_ARG)
+    cw = _cw_args()
+    _expect(lib.pa_reshape_and_cache(*(ctypes.byref(x) for x in cw),
+                                     ctypes.byref(PaLaunch(None, None, 0, 0, 0, FAKE + 2))),
+            _lib.PA_ERR_INVALID_ARG)
