@@ -363,7 +363,9 @@ def bench_prefill(args) -> int:
     cal_dst = torch.empty_like(cal_src)
     cal_dst.copy_(cal_src)
     del cal_src, cal_dst
-    mq = rows.max_query_len
+    # max_query_len sizes the grid (query-tile ranks); a smaller value makes
+    # each workgroup walk several row tiles of its (sequence, head)
+    mq = args.max_query_len if args.max_query_len > 0 else rows.max_query_len
     stream = torch.cuda.current_stream()
 
     def step_write():
@@ -429,6 +431,7 @@ def bench_prefill(args) -> int:
             "seq_lens": list(map(str, c.lengths)),
             "new_tokens": list(map(str, news)),
             "query_rows": rows.num_rows,
+            "max_query_len_arg": mq,
             "q_dtype": c.q_dtype,
             "kv_dtype": c.kv_dtype,
             "flops_per_step": flops,
@@ -477,6 +480,8 @@ def main() -> int:
                     help="event-time the attention launch of every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-query-len", type=int, default=0,
+                    help="prefill: max_query_len passed to pa_prefill (sizes its grid; 0 = the true maximum)")
     ap.add_argument("--op", default="decode", choices=["decode", "prefill", "swap"],
                     help="decode: the decode hot path (default); prefill: causal prefill of "
                          "new tokens over the cache (--config p1 | p2); swap: the batch's KV "
