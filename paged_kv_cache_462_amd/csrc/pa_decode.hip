@@ -390,6 +390,10 @@ template <int QK, int KVK, int D>
 __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodeParams p) {
   constexpr bool kBF16 = QK == K_BF16;
   constexpr bool kFP8 = KVK == K_FP8;
+  // P x V runs in bf16 (P as hi + lo parts) only for bf16 V; fp8 V decodes
+  // to f16 exactly (every E4M3 value is an f16 value), so with an fp8 cache
+  // it runs in f16 with f16 P, one product, whatever the query type
+  constexpr bool kPVBF16 = kBF16 && !kFP8;
   constexpr int ESZ = kFP8 ? 1 : 2;
   constexpr int RB = D * ESZ;          // bytes of one token's head row
   constexpr int LR = RB / 16;          // 16-byte chunks per row
@@ -408,6 +412,13 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
   // in-flight tile's LDS writes from the current tile's reads
   __shared__ i32x4 kt0[kMaxWaves][SLOTS];
   __shared__ i32x4 kt1[kMaxWaves][SLOTS];
+  // fp8 V goes through LDS as well: its per-lane register loads would be 8
+  // bytes (8 dims of a token), half a 16-byte load, so V would cost as many
+  // load instructions as K for half the bytes; load-to-LDS moves 1 KiB per
+  // instruction and the lanes read their 8 bytes back after the tile's wait
+  constexpr bool kVLds = kFP8;
+  __shared__ i32x4 vt0[kVLds ? kMaxWaves : 1][kVLds ? SLOTS : 1];
+  __shared__ i32x4 vt1[kVLds ? kMaxWaves : 1][kVLds ? SLOTS : 1];
   __shared__ int s_pref[kBalancedMaxBatch + 1];
   __shared__ int s_wtot[kMaxWaves];
 
@@ -444,6 +455,15 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
   uint32_t voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)((4 * g + i) * rs + n * VBYTES);
+  // fp8 V to LDS: instruction j, lane l loads chunk l % LR of row
+  // j*TPI + l/LR into slot j*64 + l (rows unswizzled: slot tt*LR + c holds
+  // chunk c of row tt); lane (n, g) reads its VBYTES of token 4g+i back
+  uint32_t vdma[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) vdma[j] = (uint32_t)((j * TPI + lane / LR) * rs + (lane % LR) * 16);
+  int vrd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) vrd[i] = (4 * g + i) * RB + n * VBYTES;
 
   struct Regs {
     Bytes<VBYTES> v[4];
@@ -466,14 +486,19 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
     }
 
     int ids = 0;
-    auto load_tile = [&](int i, i32x4* kt, Regs& r) {
+    auto load_tile = [&](int i, i32x4* kt, i32x4* vt, Regs& r) {
       const int64_t tb = tile_base(p, wk, i, ids, blk_bytes, rs);
       const char* kb = kbase + tb;
       const char* vb = vbase + tb;
 #pragma unroll
       for (int j = 0; j < NK; ++j) load_lds16(kb + kdma[j], kt + j * 64);
+      if constexpr (kVLds) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) r.v[q] = load_bytes<VBYTES>(vb, voff[q]);
+        for (int j = 0; j < NK; ++j) load_lds16(vb + vdma[j], vt + j * 64);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.v[q] = load_bytes<VBYTES>(vb, voff[q]);
+      }
     };
 
     float m = kMaxFloor;
@@ -482,11 +507,17 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
 #pragma unroll
     for (int j = 0; j < NJV; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // K operand chunks of the tile in LDS
+    // K operand chunks of the tile in LDS (and fp8 V's bytes)
     i32x4 kreg[NR];
-    auto fetch_tile = [&](const i32x4* kt) {
+    Bytes<VBYTES> vreg[4];
+    auto fetch_tile = [&](const i32x4* kt, const i32x4* vt) {
 #pragma unroll
       for (int rr = 0; rr < NR; ++rr) kreg[rr] = kt[kslot[rr]];
+      if constexpr (kVLds) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          vreg[q] = *reinterpret_cast<const Bytes<VBYTES>*>(reinterpret_cast<const char*>(vt) + vrd[q]);
+      }
     };
 
     auto compute_tile = [&](int i, Regs& r) {
@@ -542,11 +573,11 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
       // as hi + lo, two bf16 values whose sum carries 16 bits, and the
       // product runs twice.  The denominator sums the same rounded weights
       // the product uses.
-      const uint32_t pw0 = kBF16 ? pack_bf16(p0, p1) : pack_f16(p0, p1);
-      const uint32_t pw1 = kBF16 ? pack_bf16(p2, p3) : pack_f16(p2, p3);
+      const uint32_t pw0 = kPVBF16 ? pack_bf16(p0, p1) : pack_f16(p0, p1);
+      const uint32_t pw1 = kPVBF16 ? pack_bf16(p2, p3) : pack_f16(p2, p3);
       float ps;
       i32x2 pop_lo = {0, 0};
-      if constexpr (kBF16) {
+      if constexpr (kPVBF16) {
         const float h0 = bf16_lo(pw0), h1 = bf16_hi(pw0), h2 = bf16_lo(pw1), h3 = bf16_hi(pw1);
         const uint32_t lw0 = pack_bf16(p0 - h0, p1 - h1);
         const uint32_t lw1 = pack_bf16(p2 - h2, p3 - h3);
@@ -566,7 +597,7 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int k = 0; k < VBYTES / 4; ++k) rw[q][k] = r.v[q].w(k);
+        for (int k = 0; k < VBYTES / 4; ++k) rw[q][k] = kVLds ? vreg[q].w(k) : r.v[q].w(k);
       if (partial) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -586,8 +617,8 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
             const uint32_t sel = h ? 0x07030602u : 0x05010400u;
             const uint32_t x0 = __builtin_amdgcn_perm(rw[1][k], rw[0][k], sel);
             const uint32_t x1 = __builtin_amdgcn_perm(rw[3][k], rw[2][k], sel);
-            const i32x2 c0 = kBF16 ? fp8x4_to_bf16x4(x0) : fp8x4_to_f16x4(x0);
-            const i32x2 c1 = kBF16 ? fp8x4_to_bf16x4(x1) : fp8x4_to_f16x4(x1);
+            const i32x2 c0 = fp8x4_to_f16x4(x0);
+            const i32x2 c1 = fp8x4_to_f16x4(x1);
             a0[4 * k + 2 * h] = (uint32_t)c0[0];
             a0[4 * k + 2 * h + 1] = (uint32_t)c0[1];
             a1[4 * k + 2 * h] = (uint32_t)c1[0];
@@ -604,8 +635,8 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
       }
 #pragma unroll
       for (int j = 0; j < NJV; ++j) {
-        acc[j] = mfma_k16<kBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop, acc[j]);
-        if constexpr (kBF16) acc[j] = mfma_k16<kBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop_lo, acc[j]);
+        acc[j] = mfma_k16<kPVBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop, acc[j]);
+        if constexpr (kPVBF16) acc[j] = mfma_k16<kPVBF16>(i32x2{(int)a0[j], (int)a1[j]}, pop_lo, acc[j]);
       }
     };
 
@@ -614,9 +645,10 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
     {
       Regs r0, r1;
       run_tiles_lds(
-          p, wk, ids, [&](int i) { load_tile(i, kt0[w], r0); },
-          [&](int i) { load_tile(i, kt1[w], r1); }, [&]() { fetch_tile(kt0[w]); },
-          [&]() { fetch_tile(kt1[w]); }, [&](int i) { compute_tile(i, r0); },
+          p, wk, ids, [&](int i) { load_tile(i, kt0[w], vt0[kVLds ? w : 0], r0); },
+          [&](int i) { load_tile(i, kt1[w], vt1[kVLds ? w : 0], r1); },
+          [&]() { fetch_tile(kt0[w], vt0[kVLds ? w : 0]); },
+          [&]() { fetch_tile(kt1[w], vt1[kVLds ? w : 0]); }, [&](int i) { compute_tile(i, r0); },
           [&](int i) { compute_tile(i, r1); });
     }
 
