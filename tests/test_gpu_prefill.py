@@ -254,3 +254,33 @@ def test_prefill_bf16_wide_values_are_redone():
     assert set(np.unique(flags)) == {0, 1}, np.unique(flags)   # some flagged, some not
     atol, rtol = G.tol_for(wl)
     G.assert_close(out, ref, atol, rtol, what="prefill bf16 wide values")
+
+
+@pytest.mark.parametrize("value,flagged", [(65280.0, False), (-65280.0, False), (65536.0, True),
+                                           (-65536.0, True)])
+def test_prefill_bf16_f16_range_boundary(value, flagged):
+    """The largest bf16 magnitude below 2^16 (65280) stays on the f16 path
+    (exact in f16, no workgroup flagged); 2^16 is flagged and redone in
+    bf16.  Both against the oracle."""
+    base, lens, news = SMALL["gqa_bf16"]
+    cfg = shrink(base, batch=len(lens), lengths=("list", lens), pool_blocks=0)
+    wl = make_workload(cfg, seed=207)
+    v = wl.tok_value.float().clone()
+    v[700] = value          # one token of sequence 0, every head and dim
+    wl = type(wl)(**{**wl.__dict__, "tok_value": v.to(torch.bfloat16)})
+    rows = make_prefill_rows(wl, news, seed=208)
+    G.say(f"prefill bf16 range boundary {value}")
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_prefill(wl, kc, vc, rows)
+    d = G.to_device(wl)
+    ws = _ws(wl, rows)
+    c = wl.cfg
+    q = rows.query.to("cuda")
+    qsl = torch.from_numpy(rows.query_start_loc).to("cuda")
+    out = torch.empty_like(q)
+    pa.prefill(out, q, d.kc, d.vc, d.tables, d.lens, qsl, rows.max_query_len, wl.scale,
+               c.block_size, c.num_kv_heads, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool((ws > 0).any()) == flagged
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(out, ref, atol, rtol, what=f"prefill bf16 boundary {value}")
