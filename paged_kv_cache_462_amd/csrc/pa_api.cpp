@@ -152,7 +152,7 @@ int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Pl
     // automatic: equal shares of the batch's tiles per workgroup
     p.sched = pa::kSchedBalanced;
     p.split = 1;
-    p.slots = (int64_t)pa::kBalancedWorkgroups + B;
+    p.slots = (int64_t)pa::kBalancedSlots + B;
   } else {
     const int pt = req == 0 ? 512 : req;  // automatic fallback: 512-token partitions
     if (pt == -1 || pt >= max_ctx) {
@@ -282,10 +282,12 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   const int64_t units = Hkv * (int64_t)p.head_tiles;
   if (units > 0x7FFFFFFFLL) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   p.units = (int)units;
-  p.waves = (int)(units < pa::decode_max_waves() ? units : pa::decode_max_waves());
   {
+    int max_waves, workgroups;
+    pa::decode_launch_shape(v, &max_waves, &workgroups);
+    p.waves = (int)(units < max_waves ? units : max_waves);
     const int chunks = (p.units + p.waves - 1) / p.waves;
-    const int nwc = pa::kBalancedWorkgroups / chunks;
+    const int nwc = workgroups / chunks;
     p.nwc = nwc < 1 ? 1 : nwc;
   }
   p.sched = plan.sched;

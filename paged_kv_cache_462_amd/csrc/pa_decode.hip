@@ -387,7 +387,8 @@ __device__ __forceinline__ int64_t triple_index(const DecodeParams& p, int slot,
 // of up to 16 query heads of one kv group.
 // ============================================================================
 template <int QK, int KVK, int D>
-__global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void decode_mfma_kernel(
+    const DecodeParams p) {
   constexpr bool kBF16 = QK == K_BF16;
   constexpr bool kFP8 = KVK == K_FP8;
   // P x V runs in bf16 (P as hi + lo parts) only for bf16 V; fp8 V decodes
@@ -408,17 +409,20 @@ __global__ __launch_bounds__(kMaxThreads) void decode_mfma_kernel(const DecodePa
   static_assert(NK >= 1 && NR >= 1 && (kFP8 ? 2 * NR == NJQ : NR == NJQ), "shape");
   static_assert(VBYTES == 16 || VBYTES == 8 || VBYTES == 4, "shape");
 
+  // waves per workgroup at most (the fp8 kernel runs 4-wave workgroups,
+  // three per CU)
+  constexpr int WMAX = kFP8 ? kFp8Waves : kMaxWaves;
   // two K tiles per wave, in two arrays so the compiler can tell the
   // in-flight tile's LDS writes from the current tile's reads
-  __shared__ i32x4 kt0[kMaxWaves][SLOTS];
-  __shared__ i32x4 kt1[kMaxWaves][SLOTS];
+  __shared__ i32x4 kt0[WMAX][SLOTS];
+  __shared__ i32x4 kt1[WMAX][SLOTS];
   // fp8 V goes through LDS as well: its per-lane register loads would be 8
   // bytes (8 dims of a token), half a 16-byte load, so V would cost as many
   // load instructions as K for half the bytes; load-to-LDS moves 1 KiB per
   // instruction and the lanes read their 8 bytes back after the tile's wait
   constexpr bool kVLds = kFP8;
-  __shared__ i32x4 vt0[kVLds ? kMaxWaves : 1][kVLds ? SLOTS : 1];
-  __shared__ i32x4 vt1[kVLds ? kMaxWaves : 1][kVLds ? SLOTS : 1];
+  __shared__ i32x4 vt0[kVLds ? WMAX : 1][kVLds ? SLOTS : 1];
+  __shared__ i32x4 vt1[kVLds ? WMAX : 1][kVLds ? SLOTS : 1];
   __shared__ int s_pref[kBalancedMaxBatch + 1];
   __shared__ int s_wtot[kMaxWaves];
 
@@ -1090,8 +1094,10 @@ hipError_t launch_valu(const DecodeParams& p, int gt, dim3 grid, dim3 block, hip
 
 template <int QK, int KVK, int D>
 hipError_t launch_all(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {
-  if (p.waves < 1 || p.waves > kMaxWaves) return hipErrorInvalidValue;
-  if (p.sched == kSchedBalanced && (p.B > kBalancedMaxBatch || p.nwc < 1 || p.nwc > kBalancedWorkgroups))
+  int max_waves, workgroups;
+  decode_launch_shape(v, &max_waves, &workgroups);
+  if (p.waves < 1 || p.waves > max_waves) return hipErrorInvalidValue;
+  if (p.sched == kSchedBalanced && (p.B > kBalancedMaxBatch || p.nwc < 1 || p.nwc > kBalancedSlots))
     return hipErrorInvalidValue;
   const int chunks = (p.units + p.waves - 1) / p.waves;
   const dim3 grid = p.sched == kSchedBalanced ? dim3(chunks, p.nwc, 1) : dim3(chunks, p.num_parts, p.B);
@@ -1133,7 +1139,11 @@ bool decode_variant_built(const DecodeVariant& v) {
   return false;
 }
 
-int decode_max_waves() { return kMaxWaves; }
+void decode_launch_shape(const DecodeVariant& v, int* max_waves, int* workgroups) {
+  const bool fp8_mfma = v.path == 2 && v.kvkind == K_FP8;
+  *max_waves = fp8_mfma ? kFp8Waves : kMaxWaves;
+  *workgroups = fp8_mfma ? kBalancedWorkgroupsFp8 : kBalancedWorkgroups;
+}
 
 hipError_t launch_decode(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {
   if (!decode_variant_built(v)) return hipErrorNotSupported;

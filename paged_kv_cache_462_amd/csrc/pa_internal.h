@@ -25,6 +25,13 @@ enum Flag : int { kFlagBlockId = 0, kFlagLength = 1, kFlagSlot = 2, kFlagQuerySt
 // sized for this many) and the largest batch it takes (the per-sequence
 // tile offsets live in LDS).
 constexpr int kBalancedWorkgroups = 256;
+// The fp8 matrix-core kernel's registers and LDS leave room for three waves
+// per SIMD: it runs 4-wave workgroups, three per CU (768 in all), which
+// hides its per-tile latency better than two 8-wave waves per SIMD do.
+constexpr int kFp8Waves = 4;
+constexpr int kBalancedWorkgroupsFp8 = 768;
+// Shares per unit chunk the workspace holds slots for (the larger grid).
+constexpr int kBalancedSlots = kBalancedWorkgroupsFp8;
 constexpr int kBalancedMaxBatch = 2048;
 
 // Everything the decode kernels read, resolved on the host.
@@ -114,7 +121,8 @@ hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t stream);
 // Variants built into this library (for pa_build_info / validation).
 bool decode_variant_built(const DecodeVariant& v);
 
-// Largest number of work units (waves) one decode workgroup holds.
-int decode_max_waves();
+// Launch shape of a decode variant: waves per workgroup at most, and the
+// balanced schedule's workgroups in all.
+void decode_launch_shape(const DecodeVariant& v, int* max_waves, int* workgroups);
 
 }  // namespace pa

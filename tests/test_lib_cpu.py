@@ -158,7 +158,9 @@ def test_plan():
     # automatic: balanced shares of the batch's tiles
     rc, info = _plan(32, 32, 32, 128, 16, 128, 0)
     assert rc == 0 and info.schedule == B_ and info.partition_tokens == 0
-    slots = 256 + 32
+    # shares per unit chunk the workspace holds: 768 (the fp8 kernel's grid
+    # of 4-wave workgroups) + one per sequence
+    slots = 768 + 32
     assert info.workspace_bytes == slots * 32 * 130 * 4 + 32 * 8
     assert lib.pa_decode_workspace_bytes(32, 32, 32, 128, 16, 128, 0) == info.workspace_bytes
     # automatic with a batch beyond the balanced limit: 512-token partitions

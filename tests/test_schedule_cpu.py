@@ -1,18 +1,20 @@
 """The balanced decode schedule's arithmetic, restated on the CPU.
 
 The kernel deals the batch's 16-token tiles (sequences back to back) to NW
-workgroups as [floor(w T / NW), floor((w + 1) T / NW)) with NW = min(256, T),
-and gives piece k of sequence b the triple slot owner(S_b) + b + k.  These
-checks hold that arithmetic to its invariants on many length mixes: every
-tile is covered once, the pieces of a sequence go to consecutive workgroups
-with non-empty shares, and slots are unique and below 256 + B (the
-workspace size pa_decode_plan reports)."""
+workgroups as [floor(w T / NW), floor((w + 1) T / NW)) with NW = min(nwc, T)
+(nwc: 256 / unit chunks for 8-wave workgroups, 768 / unit chunks for the fp8
+kernel's 4-wave ones), and gives piece k of sequence b the triple slot
+owner(S_b) + b + k.  These checks hold that arithmetic to its invariants on
+many length mixes and both grid sizes: every tile is covered once, the pieces
+of a sequence go to consecutive workgroups with non-empty shares, and slots
+are unique and below 768 + B (the workspace size pa_decode_plan reports)."""
 
 import numpy as np
 import pytest
 
 TILE = 16
 NWC = 256
+SLOTS = 768   # shares per unit chunk the workspace holds slots for
 
 
 def schedule(lengths, nwc=NWC):
@@ -42,8 +44,8 @@ def schedule(lengths, nwc=NWC):
     return out, T, NW
 
 
-def _check(lengths):
-    pieces, T, NW = schedule(lengths)
+def _check(lengths, nwc=NWC):
+    pieces, T, NW = schedule(lengths, nwc)
     B = len(lengths)
     covered = {}
     slots = set()
@@ -56,7 +58,7 @@ def _check(lengths):
         by_seq.setdefault(b, []).append((wi, a, e, slot))
         if slot >= 0:
             assert slot not in slots
-            assert 0 <= slot < NWC + B
+            assert 0 <= slot < SLOTS + B
             slots.add(slot)
     for b, L in enumerate(lengths):
         nt = (int(L) + TILE - 1) // TILE
@@ -73,8 +75,9 @@ def _check(lengths):
     assert len(covered) == T
 
 
+@pytest.mark.parametrize("nwc", [256, 64, 768, 384])
 @pytest.mark.parametrize("seed", range(40))
-def test_balanced_schedule_invariants(seed):
+def test_balanced_schedule_invariants(seed, nwc):
     rng = np.random.default_rng(seed)
     B = int(rng.choice([1, 2, 3, 7, 31, 64, 255, 256, 257, 600, 2048]))
     kind = seed % 4
@@ -86,7 +89,7 @@ def test_balanced_schedule_invariants(seed):
         L = np.clip(np.rint(np.exp(rng.normal(7, 1, B))), 16, 16384)
     else:
         L = rng.integers(0, 3, B) * rng.integers(1, 5000, B)  # many zeros
-    _check([int(x) for x in L])
+    _check([int(x) for x in L], nwc)
 
 
 def test_balanced_schedule_edges():
