@@ -319,7 +319,8 @@ int64_t pa_decode_workspace_bytes(int32_t batch, int32_t num_q_heads,
 #define PA_SCHEDULE_SINGLE 0     /* one workgroup per sequence                 */
 #define PA_SCHEDULE_PARTITIONS 1 /* fixed-size token partitions, then a merge  */
 #define PA_SCHEDULE_BALANCED 2   /* equal shares of the batch's 16-token tiles
-                                    per workgroup (256 workgroups in all), found
+                                    per workgroup (256 in all; 768 smaller ones
+                                    for an fp8 cache on the matrix cores), found
                                     on the device from seq_lens; sequences cut
                                     by a share boundary are merged afterwards */
 
