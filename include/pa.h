@@ -257,7 +257,10 @@ int64_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t n
  *                 must be 0 (the plan is always the balanced schedule, so
  *                 the batch is at most 2048 sequences)
  * Supported head_dim: 64, 128.  Three launches (prefix pass, decode of the
- * rest, merge), deterministic.
+ * rest, merge), deterministic.  It pays when the prefix is most of most
+ * sequences; when many sequences end inside the prefix, the prefix pass and
+ * the merge of its pieces cost more than they save and pa_decode is the
+ * faster call.  The lengths stay on the device, so the caller chooses.
  */
 int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query,
                             const pa_tensor* key_cache, const pa_tensor* value_cache,
