@@ -198,3 +198,51 @@ def test_prefill_mutants_are_caught(monkeypatch, attr, mutant):
         except (AssertionError, IndexError, ValueError):
             failed += 1
     assert failed >= 1
+
+
+# --- the storage-format decode oracle (paged_decode_stored) -----------------
+
+from oracle import cache_write as OW  # noqa: E402
+from tests import test_oracle_decode_stored as TS  # noqa: E402
+
+_real_stored = A.paged_decode_stored
+
+
+def _swapped_scales(query, kc, vc, kind, k_scale, v_scale, *rest, **kw):
+    return _real_stored(query, kc, vc, kind, v_scale, k_scale, *rest, **kw)
+
+
+def _k_scale_on_both(query, kc, vc, kind, k_scale, v_scale, *rest, **kw):
+    return _real_stored(query, kc, vc, kind, k_scale, k_scale, *rest, **kw)
+
+
+def _pairs_ignored(*args, **kw):
+    if len(args) > 10:
+        args = args[:10]
+    kw.pop("pairs", None)
+    return _real_stored(*args, **kw)
+
+
+def _no_dequant_scale(t, kind, scale=1.0):
+    from oracle import fp8 as F
+    if kind == "fp8":
+        return F.decode(t.numpy(), 1.0)
+    return t.to(torch.float64).numpy()
+
+
+@pytest.mark.parametrize("patch,pin", [
+    ((A, "paged_decode_stored", _swapped_scales), TS.fp8_pin),
+    ((A, "paged_decode_stored", _k_scale_on_both), TS.fp8_pin),
+    ((A, "paged_decode_stored", _pairs_ignored), TS.subset_pin),
+    ((A, "kv_head_for", _wrong_kv_head), TS.gqa_pin),
+    ((OW, "to_f64", _no_dequant_scale), TS.fp8_pin),
+])
+def test_stored_decode_mutants_are_caught(monkeypatch, patch, pin):
+    """Scales swapped, V dequantised with K's scale, the scale dropped, the
+    pairs subset ignored, interleaved kv heads: each fails a pin of
+    paged_decode_stored."""
+    pin()
+    target, attr, mutant = patch
+    monkeypatch.setattr(target, attr, mutant)
+    with pytest.raises((AssertionError, IndexError)):
+        pin()
