@@ -34,6 +34,11 @@ Pins (tests/test_oracle_attention.py): torch's scaled_dot_product_attention
 in fp64 on the unpaged K/V, a pure-Python brute force on tiny shapes, closed
 forms (one token, constant values, zero query), invariance under permuting
 physical blocks, NaN-poisoned unused slots, and O2 == O1 to 1e-12.
+paged_decode_stored (tests/test_oracle_decode_stored.py): caches built and
+decoded by hand (torch's float8_e4m3fn conversion times each tensor's own
+scale) against torch's scaled_dot_product_attention in fp64, fp8 with
+distinct K and V scales, GQA, a zero-length row, a `pairs` subset; bit-equal
+to O1 for 32- and 16-bit storage.
 """
 
 from __future__ import annotations
