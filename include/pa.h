@@ -364,6 +364,9 @@ typedef struct pa_allocator pa_allocator;
  * NULL for 0..N-1 (the first allocation then returns N-1).  Returns NULL on
  * invalid arguments (see pa_last_error). */
 pa_allocator* pa_alloc_create(int32_t num_blocks, const int32_t* free_order);
+/* The handle is dead after this call.  Block managers and prefix caches
+ * built on the allocator may still be destroyed afterwards (in any order):
+ * its memory is released when the last of them is. */
 void pa_alloc_destroy(pa_allocator* a);
 /* PA_ERR_OUT_OF_BLOCKS when the stack is empty. */
 int pa_alloc_allocate(pa_allocator* a, int32_t* block_out);
@@ -446,6 +449,31 @@ int32_t pa_pc_insert(pa_prefix_cache* c, const int32_t* tokens, int64_t n_tokens
 int32_t pa_pc_evict(pa_prefix_cache* c, int32_t max_blocks);
 /* Number of cached blocks. */
 int32_t pa_pc_size(const pa_prefix_cache* c);
+
+/*
+ * pa_bm_add_sequence_cached -- admit a new sequence through the prefix cache
+ * ("5.KV Cache 管理 & PagedAttention", question 20, allocate_with_prefix:
+ * the new table starts with the cached blocks of the longest matching
+ * prefix, each with one more reference, blocks are allocated for the
+ * remaining tokens, and the sequence's prefix is cached in turn;
+ * "KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践",
+ * `HashBasedCaching` walk-through).  tokens[0 .. n_tokens) are the
+ * sequence's token ids.  Steps: pa_pc_match; pa_bm_add_sequence with the
+ * matched blocks (the match's own references are then released);
+ * pa_bm_append_slot for every remaining token; pa_pc_insert of the
+ * sequence's full blocks.  m and c must share one allocator and one block
+ * size.
+ *   slots_out  [n_tokens - matched] i64 (host): the cache slot of every
+ *              token that was not found, in position order -- the K/V the
+ *              caller writes with pa_reshape_and_cache before any call
+ *              reads this sequence (or another that matches its blocks)
+ * Returns the number of matched tokens (a multiple of the block size), or
+ * a negative status; on PA_ERR_OUT_OF_BLOCKS (or any error after the
+ * sequence was added) the sequence is removed again and every reference
+ * it took is released.  Plain CPU code.
+ */
+int64_t pa_bm_add_sequence_cached(pa_block_manager* m, pa_prefix_cache* c, int64_t seq_id,
+                                  const int32_t* tokens, int64_t n_tokens, int64_t* slots_out);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     lib_path,
     load,
 )
+from .batch import AdmittedBatch, admit_with_shared_prompt  # noqa: F401
 from .ops import (  # noqa: F401
     PATH_AUTO,
     PATH_MFMA,

@@ -97,6 +97,8 @@ SIGNATURES = {
     "pa_pc_insert": (c_int32, [_P, POINTER(c_int32), c_int64, POINTER(c_int32), c_int32]),
     "pa_pc_evict": (c_int32, [_P, c_int32]),
     "pa_pc_size": (c_int32, [_P]),
+    "pa_bm_add_sequence_cached": (c_int64, [_M, _P, c_int64, POINTER(c_int32), c_int64,
+                                            POINTER(c_int64)]),
 }
 
 _LIB = None

@@ -22,6 +22,8 @@
 
 namespace pa {
 int set_error(int code, const char* msg);
+void alloc_add_user(pa_allocator* a);
+void alloc_drop_user(pa_allocator* a);
 }
 
 struct pa_allocator {
@@ -29,6 +31,13 @@ struct pa_allocator {
   int32_t n = 0;
   std::vector<int32_t> free_stack;  // top = back()
   std::vector<int32_t> ref;
+  // Managers and prefix caches built on this allocator release references
+  // through it when they are destroyed, so its memory outlives them: a
+  // destroy request while any of them lives only marks it, and the last one
+  // to go frees it (callers such as garbage collectors may destroy the
+  // three in any order).
+  int32_t users = 0;
+  bool doomed = false;
 };
 
 struct pa_block_manager {
@@ -97,7 +106,17 @@ pa_allocator* pa_alloc_create(int32_t num_blocks, const int32_t* free_order) {
   return a;
 }
 
-void pa_alloc_destroy(pa_allocator* a) { delete a; }
+void pa_alloc_destroy(pa_allocator* a) {
+  if (!a) return;
+  {
+    std::lock_guard<std::mutex> g(a->mu);
+    if (a->users > 0) {
+      a->doomed = true;
+      return;
+    }
+  }
+  delete a;
+}
 
 int pa_alloc_allocate(pa_allocator* a, int32_t* block_out) {
   if (!a || !block_out) return pa::set_error(PA_ERR_INVALID_ARG, "null argument");
@@ -146,10 +165,16 @@ pa_block_manager* pa_bm_create(pa_allocator* a, int32_t block_size) {
   pa_block_manager* m = new pa_block_manager;
   m->a = a;
   m->bs = block_size;
+  pa::alloc_add_user(a);
   return m;
 }
 
-void pa_bm_destroy(pa_block_manager* m) { delete m; }
+void pa_bm_destroy(pa_block_manager* m) {
+  if (!m) return;
+  pa_allocator* a = m->a;
+  delete m;
+  pa::alloc_drop_user(a);
+}
 
 int pa_bm_add_sequence(pa_block_manager* m, int64_t seq_id, const int32_t* shared_blocks,
                        int32_t n_shared, int64_t shared_tokens) {
@@ -268,3 +293,24 @@ int pa_bm_export(const pa_block_manager* m, const int64_t* seq_ids, int32_t n, i
 }
 
 }  // extern "C"
+
+namespace pa {
+// block size of a manager (for the prefix-cache admission, which must use
+// the same one)
+int32_t bm_block_size(const pa_block_manager* m) { return m ? m->bs : 0; }
+
+void alloc_add_user(pa_allocator* a) {
+  std::lock_guard<std::mutex> g(a->mu);
+  ++a->users;
+}
+
+// the allocator is freed here when it was destroyed while this user lived
+void alloc_drop_user(pa_allocator* a) {
+  bool free_it;
+  {
+    std::lock_guard<std::mutex> g(a->mu);
+    free_it = --a->users == 0 && a->doomed;
+  }
+  if (free_it) delete a;
+}
+}  // namespace pa

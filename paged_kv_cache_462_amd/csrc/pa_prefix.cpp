@@ -34,6 +34,9 @@
 
 namespace pa {
 int set_error(int code, const char* msg);
+int32_t bm_block_size(const pa_block_manager* m);
+void alloc_add_user(pa_allocator* a);
+void alloc_drop_user(pa_allocator* a);
 }
 
 namespace {
@@ -110,6 +113,7 @@ pa_prefix_cache* pa_pc_create(pa_allocator* a, int32_t block_size) {
   pa_prefix_cache* c = new pa_prefix_cache;
   c->a = a;
   c->bs = block_size;
+  pa::alloc_add_user(a);
   return c;
 }
 
@@ -117,7 +121,9 @@ void pa_pc_destroy(pa_prefix_cache* c) {
   if (!c) return;
   for (const Node& n : c->nodes)
     if (n.live) pa_alloc_decref(c->a, n.block);
+  pa_allocator* a = c->a;
   delete c;
+  pa::alloc_drop_user(a);
 }
 
 int32_t pa_pc_match(pa_prefix_cache* c, const int32_t* tokens, int64_t n_tokens,
@@ -225,3 +231,49 @@ int32_t pa_pc_size(const pa_prefix_cache* c) {
 }
 
 }  // extern "C"
+
+// Admission of a new sequence through the prefix cache ("5.KV Cache 管理 &
+// PagedAttention", question 20, allocate_with_prefix: the table starts with
+// the matched blocks, each with one more reference; blocks are allocated
+// for the remaining tokens; the sequence's prefix is then cached).  Built on
+// the public calls above and the block manager's, so the locking stays
+// theirs: match, attach the matched blocks to the new sequence, release the
+// match's own references, reserve a slot per remaining token, offer the
+// sequence's full blocks to the cache.
+extern "C" int64_t pa_bm_add_sequence_cached(pa_block_manager* m, pa_prefix_cache* c,
+                                             int64_t seq_id, const int32_t* tokens,
+                                             int64_t n_tokens, int64_t* slots_out) {
+  if (!m || !c || n_tokens < 0 || (n_tokens > 0 && (!tokens || !slots_out)))
+    return pa::set_error(PA_ERR_INVALID_ARG, "invalid arguments");
+  if (n_tokens > 0x7FFFFFFFLL) return pa::set_error(PA_ERR_INVALID_ARG, "sequence too long");
+  const int32_t bs = c->bs;
+  if (pa::bm_block_size(m) != bs)
+    return pa::set_error(PA_ERR_INVALID_ARG, "block manager and prefix cache block sizes differ");
+  const int32_t full = (int32_t)(n_tokens / bs);
+  std::vector<int32_t> matched((size_t)full + 1);
+  const int32_t k = pa_pc_match(c, tokens, n_tokens, matched.data(), full);
+  if (k < 0) return k;
+  int rc = pa_bm_add_sequence(m, seq_id, matched.data(), k, (int64_t)k * bs);
+  // the sequence took its own references (or failed): drop the match's
+  for (int32_t i = 0; i < k; ++i) pa_alloc_decref(c->a, matched[i]);
+  if (rc) return rc;
+  const int64_t first = (int64_t)k * bs;
+  for (int64_t t = first; t < n_tokens; ++t) {
+    int32_t src, dst;
+    rc = pa_bm_append_slot(m, seq_id, &slots_out[t - first], &src, &dst);
+    if (rc) {
+      pa_bm_free_sequence(m, seq_id);  // back to the state before the call
+      return rc;
+    }
+  }
+  const int32_t nb = pa_bm_num_blocks_of(m, seq_id);
+  std::vector<int32_t> table((size_t)(nb > 0 ? nb : 1));
+  int32_t len32 = 0;
+  rc = pa_bm_export(m, &seq_id, 1, nb, table.data(), &len32);
+  if (rc == PA_OK) rc = pa_pc_insert(c, tokens, n_tokens, table.data(), nb);
+  if (rc < 0) {
+    pa_bm_free_sequence(m, seq_id);
+    return rc;
+  }
+  return first;
+}

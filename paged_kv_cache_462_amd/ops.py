@@ -73,6 +73,19 @@ def _launch(ref: torch.Tensor, workspace: Optional[torch.Tensor] = None,
     return ln
 
 
+def _own_workspace(nbytes: int, device: torch.device,
+                   stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+    """A workspace this module allocates for one call.  torch's caching
+    allocator ties a block to the stream current at allocation; the kernels
+    may run on another (`stream=`), so the block is also recorded on that
+    stream: it is not handed out again until the work queued there so far
+    has finished, even though the tensor is dropped when the call returns."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and ws.is_cuda:
+        ws.record_stream(stream)
+    return ws
+
+
 def _is_fp8(t: torch.Tensor, kv_dtype: Optional[str]) -> bool:
     return kv_dtype == "fp8" or t.dtype == torch.float8_e4m3fn
 
@@ -120,14 +133,15 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
            path: int = PATH_AUTO, stream: Optional[torch.cuda.Stream] = None,
            error_flags: Optional[torch.Tensor] = None) -> None:
     """pa_decode.  When the plan splits and no workspace is given, one is
-    allocated here (torch owns it); pass `workspace` to avoid that."""
+    allocated here (torch owns it, and it is recorded on `stream`); pass
+    `workspace` to avoid that."""
     fp8 = _is_fp8(key_cache, kv_dtype)
     if workspace is None:
         need = decode_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
                                       query.shape[2], block_size, block_tables.shape[1],
                                       partition_tokens)
         if need > 0:
-            workspace = torch.empty(need, dtype=torch.uint8, device=query.device)
+            workspace = _own_workspace(need, query.device, stream)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens))
     ln = _launch(query, workspace, partition_tokens, path, stream, error_flags)
@@ -159,7 +173,7 @@ def decode_shared_prefix(out: torch.Tensor, query: torch.Tensor, key_cache: torc
         need = decode_shared_prefix_workspace_bytes(query.shape[0], query.shape[1], num_kv_heads,
                                                     query.shape[2], block_size,
                                                     block_tables.shape[1], prefix_tokens)
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=query.device)
+        workspace = _own_workspace(max(need, 16), query.device, stream)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
             _desc(prefix_blocks))
@@ -186,7 +200,7 @@ def prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     if workspace is None and query.dtype == torch.bfloat16 and key_cache.dtype == torch.bfloat16:
         need = prefill_workspace_bytes(seq_lens.shape[0], query.shape[1], query.shape[0],
                                        max_query_len)
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=query.device)
+        workspace = _own_workspace(max(need, 4), query.device, stream)
     args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
             _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens),
             _desc(query_start_loc))
@@ -316,6 +330,17 @@ class BlockManager:
 
     def num_blocks_of(self, seq_id: int) -> int:
         return check(self._lib.pa_bm_num_blocks_of(self._h, int(seq_id)))
+
+    def add_sequence_cached(self, cache: "PrefixCache", seq_id: int, tokens: Sequence[int]):
+        """pa_bm_add_sequence_cached: admit a sequence through the prefix
+        cache.  Returns (matched tokens, slots of the remaining tokens)."""
+        tok = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        slots = np.empty(max(len(tok), 1), dtype=np.int64)
+        k = check(self._lib.pa_bm_add_sequence_cached(
+            self._h, cache._h, int(seq_id),
+            tok.ctypes.data_as(ctypes.POINTER(c_int32)) if len(tok) else None, len(tok),
+            slots.ctypes.data_as(ctypes.POINTER(c_int64))))
+        return int(k), slots[:len(tok) - k].copy()
 
     def export(self, seq_ids: Sequence[int], max_blocks: int):
         ids = np.ascontiguousarray(np.asarray(list(seq_ids), dtype=np.int64))

@@ -51,6 +51,14 @@ class Workload:
     new_slots: np.ndarray         # [B] int64: slot of each sequence's last token, -1 if shared
     new_tok: np.ndarray           # [B] int64: index into the token stream (or -1)
     shared_blocks: np.ndarray     # [n_shared] int32 physical ids of the shared prefix
+    token_ids: List[np.ndarray]   # per sequence: its L_b token ids (int32); the
+                                  # first min(L_b, prefix) are the shared prompt's
+    prompt_rows: int              # stream rows 0 .. prompt_rows-1 hold the shared
+                                  # prompt's K/V, position order (0 without one)
+    private_row0: np.ndarray      # [B] int64: stream row of each sequence's
+                                  # first token past the shared prompt
+    pool_order: np.ndarray        # [N] int32: the seeded permutation the block
+                                  # ids were handed out in (first id first)
     k_scale: float                # fp8 per-tensor scales (1.0 otherwise)
     v_scale: float
     scale: float                  # score scale 1/sqrt(head_dim), as float32
@@ -68,6 +76,14 @@ class Workload:
 
     def new_value(self) -> torch.Tensor:
         return _gather_rows(self.tok_value, self.new_tok)
+
+    def position_rows(self, b: int, positions: np.ndarray) -> np.ndarray:
+        """Stream rows holding the K/V of sequence b at `positions`: a shared
+        prompt position reads the prompt's row (the same tokens after the
+        same history have the same K/V), a later one the sequence's own."""
+        pos = np.asarray(positions, dtype=np.int64)
+        P = self.prompt_rows
+        return np.where(pos < P, pos, self.private_row0[b] + (pos - P))
 
     def kv_bytes_per_elem(self) -> int:
         return {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[self.cfg.kv_dtype]
@@ -143,7 +159,14 @@ def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None) -> Workload:
     if cfg.shared_prefix_tokens % bs:
         raise ValueError("a shared prefix must fill whole blocks")
     n_shared = cfg.shared_prefix_tokens // bs
-    private_need = [max(0, n - n_shared) for n in need]
+    P = cfg.shared_prefix_tokens
+    # A sequence shares the prompt's blocks that it fills completely (all of
+    # them when it is longer than the prompt): a prefix cache hands out whole
+    # blocks only.  The rest of its blocks are its own; when it ends inside
+    # the prompt, its last, partly filled block is a private block holding
+    # the prompt's K/V at those positions.
+    k_shared = [min(n_shared, int(x) // bs) if int(x) < P else n_shared for x in L]
+    private_need = [n - k for n, k in zip(need, k_shared)]
     if cfg.pool_blocks:
         N = int(cfg.pool_blocks)
     else:
@@ -159,39 +182,62 @@ def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None) -> Workload:
     max_blocks = max(max(need), 1)
     tables = np.full((B, max_blocks), -1, dtype=np.int32)
     for b in range(B):
-        k = min(need[b], n_shared)
+        k = k_shared[b]
         tables[b, :k] = shared[:k]
         tables[b, k:need[b]] = perm[cursor:cursor + private_need[b]]
         cursor += private_need[b]
 
     query = _normals(rng, (B, Hq, D), cfg.q_dtype)
 
-    # Token stream: the shared prefix once (as long as the longest sequence
-    # that uses it), then every sequence's private tokens in position order.
+    # Token stream: the whole shared prompt once, then every sequence's
+    # tokens past it in position order; these rows are drawn.  After them
+    # come copies of prompt rows for the private last blocks of sequences
+    # that end inside the prompt.
     slots: List[np.ndarray] = []
-    prefix_len = 0
     if n_shared:
-        prefix_len = min(cfg.shared_prefix_tokens, int(L.max()))
-        pos = np.arange(prefix_len, dtype=np.int64)
+        pos = np.arange(P, dtype=np.int64)
         slots.append(shared[pos // bs].astype(np.int64) * bs + pos % bs)
-    first_private = n_shared * bs
     new_tok = np.full(B, -1, dtype=np.int64)
     new_slots = np.full(B, -1, dtype=np.int64)
+    private_row0 = np.zeros(B, dtype=np.int64)
     count = sum(len(s) for s in slots)
     for b in range(B):
-        start = min(first_private, int(L[b])) if n_shared else 0
+        start = min(P, int(L[b]))
         pos = np.arange(start, int(L[b]), dtype=np.int64)
         s = tables[b, pos // bs].astype(np.int64) * bs + pos % bs
         slots.append(s)
+        private_row0[b] = count
         if len(pos):
             new_tok[b] = count + len(pos) - 1
             new_slots[b] = s[-1]
         count += len(pos)
+    T = count
+    copy_src: List[np.ndarray] = []
+    for b in range(B):
+        if int(L[b]) < P and k_shared[b] < need[b]:
+            pos = np.arange(k_shared[b] * bs, int(L[b]), dtype=np.int64)
+            slots.append(tables[b, pos // bs].astype(np.int64) * bs + pos % bs)
+            copy_src.append(pos)
+            new_tok[b] = count + len(pos) - 1
+            new_slots[b] = slots[-1][-1]
+            count += len(pos)
     slot_mapping = np.concatenate(slots) if slots else np.zeros(0, np.int64)
-    T = len(slot_mapping)
 
     tok_key = _normals(rng, (T, Hkv, D), cfg.src_dtype)
     tok_value = _normals(rng, (T, Hkv, D), cfg.src_dtype)
+    if copy_src:
+        src = torch.from_numpy(np.concatenate(copy_src))
+        tok_key = torch.cat([tok_key, tok_key[src]])
+        tok_value = torch.cat([tok_value, tok_value[src]])
+
+    # token ids (for the prefix cache), from a generator of their own so the
+    # draws above do not move: the shared prompt's, then each sequence's own
+    trng = np.random.default_rng([cfg.seed if seed is None else seed, 0x70C5])
+    prompt_ids = trng.integers(1, 32000, size=P).astype(np.int32)
+    token_ids = []
+    for b in range(B):
+        own = trng.integers(1, 32000, size=max(0, int(L[b]) - P)).astype(np.int32)
+        token_ids.append(np.concatenate([prompt_ids[:min(P, int(L[b]))], own]))
 
     k_scale = v_scale = 1.0
     if cfg.kv_dtype == "fp8":
@@ -204,7 +250,8 @@ def make_workload(cfg: WorkloadConfig, seed: Optional[int] = None) -> Workload:
     return Workload(cfg=cfg, seq_lens=L, block_tables=tables, num_blocks=N,
                     query=query, tok_key=tok_key, tok_value=tok_value,
                     slot_mapping=slot_mapping, new_slots=new_slots,
-                    new_tok=new_tok, shared_blocks=shared.copy(),
+                    new_tok=new_tok, shared_blocks=shared.copy(), token_ids=token_ids,
+                    prompt_rows=P, private_row0=private_row0, pool_order=perm,
                     k_scale=k_scale, v_scale=v_scale, scale=scale)
 
 

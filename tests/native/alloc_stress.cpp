@@ -155,6 +155,53 @@ int main(int argc, char** argv) {
   CHECK(pa_alloc_incref(a, N) == PA_ERR_BAD_BLOCK);
   pa_bm_destroy(m);
   pa_alloc_destroy(a);
+
+  // admissions through the prefix cache from several threads (one shared
+  // prompt, each thread's own continuations), then teardown with the
+  // allocator destroyed first: the manager and the cache still release
+  // their references through it, and the last of them frees it
+  {
+    pa_allocator* a2 = pa_alloc_create(N, nullptr);
+    pa_block_manager* m2 = pa_bm_create(a2, bs);
+    pa_prefix_cache* c2 = pa_pc_create(a2, bs);
+    CHECK(a2 && m2 && c2);
+    std::vector<int32_t> prompt(bs * 3);
+    for (size_t i = 0; i < prompt.size(); ++i) prompt[i] = 5000 + (int)i;
+    auto admit_work = [&](int t) {
+      std::mt19937 rng(4242 + t);
+      std::vector<int64_t> seqs;
+      for (int op = 0; op < kOps / 8; ++op) {
+        std::vector<int32_t> toks(prompt.begin(), prompt.begin() + bs * (rng() % 4));
+        const int extra = (int)(rng() % (2 * bs));
+        for (int i = 0; i < extra; ++i) toks.push_back(t * 1000 + op * 40 + i);
+        std::vector<int64_t> slots(toks.size() + 1);
+        const int64_t id = (int64_t)t << 32 | op;
+        const int64_t k = pa_bm_add_sequence_cached(m2, c2, id, toks.data(), (int64_t)toks.size(),
+                                                    slots.data());
+        CHECK(k >= 0 || k == PA_ERR_OUT_OF_BLOCKS);
+        if (k >= 0) {
+          CHECK(k % bs == 0 && k <= (int64_t)toks.size());
+          CHECK(pa_bm_seq_len(m2, id) == (int64_t)toks.size());
+          seqs.push_back(id);
+        }
+        if (rng() % 3 == 0 && !seqs.empty()) {
+          CHECK(pa_bm_free_sequence(m2, seqs.front()) == PA_OK);
+          seqs.erase(seqs.begin());
+        }
+        if (rng() % 16 == 0) CHECK(pa_pc_evict(c2, 2) >= 0);
+      }
+      for (int64_t id : seqs) CHECK(pa_bm_free_sequence(m2, id) == PA_OK);
+    };
+    th.clear();
+    for (int t = 0; t < kThreads; ++t) th.emplace_back(admit_work, t);
+    for (auto& x : th) x.join();
+    CHECK(pa_pc_evict(c2, N) >= 0);
+    CHECK(pa_pc_size(c2) == 0);
+    CHECK(pa_alloc_num_free(a2) == N);
+    pa_alloc_destroy(a2);
+    pa_pc_destroy(c2);
+    pa_bm_destroy(m2);
+  }
   if (g_fail.load()) {
     std::fprintf(stderr, "%d checks failed\n", g_fail.load());
     return 1;

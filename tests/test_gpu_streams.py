@@ -121,3 +121,37 @@ def test_decode_from_host_threads():
     kc, vc = G.oracle_caches(wl)
     atol, rtol = G.tol_for(wl)
     G.assert_close(ref[0], G.oracle_decode(wl, kc, vc), atol, rtol, what="threads reference")
+
+
+def test_side_stream_without_workspace():
+    """decode on a side stream with no workspace: the binding allocates one
+    on the current stream and records it on the launch stream, so the
+    tensors the current stream allocates and fills right after the call
+    never take its memory while the kernels still use it."""
+    G.say("streams: side stream, workspace allocated by the binding")
+    wl = make_workload(shrink(get_config("c3"), batch=8, lengths=("uniform", 1000, 3000),
+                              pool_blocks=0), seed=66)
+    c = wl.cfg
+    d = G.to_device(wl)
+    need = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                     c.block_size, wl.max_blocks, 0)
+    assert need > 0
+    ref = G.gpu_decode(wl, d)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    outs, fillers = [], []
+    for _ in range(8):
+        o = torch.empty_like(d.query)
+        side.wait_stream(cur)
+        pa.decode(o, d.query, d.kc, d.vc, d.tables, d.lens, wl.scale, c.block_size,
+                  c.num_kv_heads, stream=side)
+        # the current stream takes memory of the workspace's size at once
+        # and overwrites it while the side stream is still decoding
+        for _ in range(3):
+            fillers.append(torch.full((need,), 0x7F, dtype=torch.uint8, device=d.kc.device))
+        outs.append(o)
+        cur.wait_stream(side)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(_bits(o), _bits(ref))
