@@ -50,7 +50,11 @@
 //    of the error budget of a 16-bit result).  A bf16 query therefore runs
 //    P x V in f16 with f16 P (11 bits, like the f16 query): V is converted
 //    to f16 while staged (fp8 V decodes to f16 directly), exactly for bf16
-//    values below 2^16.  A workgroup that staged a wider value is flagged
+//    magnitudes from 2^-14 up to (not including) 2^16; smaller ones land on
+//    f16's subnormal grid (spacing 2^-24), an absolute error of at most
+//    2^-25 per value and so at most 2^-25 on an output, which is a weighted
+//    mean of the values.  A workgroup that staged a value of 2^16 or more
+//    is flagged
 //    and recomputed by a second launch in bf16, P split into a high and a
 //    low bf16 part with a product each (~16 significant bits).  Without
 //    the flag array the bf16 product runs throughout.

@@ -194,3 +194,82 @@ def caches_equal(a: torch.Tensor, b: torch.Tensor) -> bool:
     """Bitwise equality (NaN payloads included)."""
     iv = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[a.element_size()]
     return bool(torch.equal(a.cpu().view(iv), b.cpu().view(iv)))
+
+
+# --- shared-prompt batches built through the host chain ------------------------
+
+@dataclass
+class Chain:
+    alloc: object
+    manager: object
+    cache: object
+    batch: object
+    slots: np.ndarray     # [T'] int64: every K/V slot the batch writes
+    rows: np.ndarray      # [T'] int64: the stream row written there
+
+
+def admit_chain(wl: Workload) -> Chain:
+    """The workload's tables through the library's allocator (handing out
+    ids in the workload's seeded order), block manager and prefix cache:
+    the shared prompt first, then every request, then the prompt's own
+    sequence released."""
+    c = wl.cfg
+    P = c.shared_prefix_tokens
+    alloc = pa.BlockAllocator(wl.num_blocks, wl.pool_order[::-1])
+    mgr = pa.BlockManager(alloc, c.block_size)
+    cache = pa.PrefixCache(alloc, c.block_size)
+    prompt = wl.token_ids[int(np.argmax(wl.seq_lens))][:P]
+    batch = pa.admit_with_shared_prompt(mgr, cache, prompt, wl.token_ids, wl.max_blocks)
+    slots, rows = [], []
+    for i, first, s in batch.writes:
+        pos = np.arange(first, first + len(s))
+        rows.append(pos if i < 0 else wl.position_rows(i, pos))
+        slots.append(s)
+    return Chain(alloc, mgr, cache, batch, np.concatenate(slots), np.concatenate(rows))
+
+
+def chain_to_device(wl: Workload, ch: Chain) -> Dev:
+    """Device buffers of the chain's batch: tables and lengths from the
+    block manager, the cache filled by pa_reshape_and_cache at the chain's
+    slots (pool poisoned elsewhere)."""
+    c = wl.cfg
+    tables, lens = ch.batch.tables, ch.batch.seq_lens
+    assert tables.shape == (c.batch, wl.max_blocks)
+    for b in range(c.batch):
+        nb = -(-int(lens[b]) // c.block_size)
+        assert (tables[b, :nb] >= 0).all() and (tables[b, :nb] < wl.num_blocks).all()
+    assert len(np.unique(ch.slots)) == len(ch.slots)
+    assert ch.slots.max() < wl.num_blocks * c.block_size
+    dev = torch.device("cuda:0")
+    shape = (wl.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    st = kv_store_dtype(wl)
+    fill = 0x7F if c.kv_dtype == "fp8" else float("nan")
+    kc = torch.full(shape, fill, dtype=st, device=dev)
+    vc = kc.clone()
+    ri = torch.from_numpy(ch.rows)
+    d = Dev(query=wl.query.to(dev), tables=torch.from_numpy(tables).to(dev),
+            lens=torch.from_numpy(lens).to(dev), slots=torch.from_numpy(ch.slots).to(dev),
+            tok_key=wl.tok_key[ri].to(dev), tok_value=wl.tok_value[ri].to(dev), kc=kc, vc=vc)
+    gpu_write(wl, d)
+    return d
+
+
+def chain_oracle_caches(wl: Workload, ch: Chain):
+    kc, vc = empty_cache_cpu(wl), empty_cache_cpu(wl)
+    ri = torch.from_numpy(ch.rows)
+    OW.reshape_and_cache(wl.tok_key[ri], wl.tok_value[ri], ch.slots, kc, vc,
+                         wl.cfg.kv_dtype, wl.k_scale, wl.v_scale)
+    return kc, vc
+
+
+def chain_oracle_decode(wl: Workload, ch: Chain, kc, vc) -> np.ndarray:
+    return OA.paged_decode_stored(wl.query, kc, vc, wl.cfg.kv_dtype, wl.k_scale, wl.v_scale,
+                                  ch.batch.tables, ch.batch.seq_lens, wl.scale,
+                                  wl.cfg.block_size)
+
+
+def err_summary(got: torch.Tensor, ref: np.ndarray, atol: float, rtol: float, what: str) -> None:
+    g = got.detach().to("cpu", torch.float64).numpy()
+    err = np.abs(g - ref)
+    say(f"{what}: {err.size} outputs, max abs err {err.max():.2e}, max err / bound "
+        f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")

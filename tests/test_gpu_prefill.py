@@ -163,8 +163,14 @@ def test_prefill_after_gpu_cache_write_of_the_chunk():
     G.assert_close(out, ref, atol, rtol, what="prefill after chunk write")
 
 
-@pytest.mark.parametrize("name", ["p1", "p2"])
-def test_prefill_full_size(name):
+def _err_report(got, ref, atol, rtol, what):
+    g = got.to(torch.float64).numpy() if isinstance(got, torch.Tensor) else got
+    err = np.abs(g - ref)
+    G.say(f"{what}: {err.size} outputs, max abs err {err.max():.2e}, max err / bound "
+          f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")
+
+
+def _full_prefill(name):
     cfg, news = get_prefill_config(name)
     wl = make_workload(cfg)
     rows = make_prefill_rows(wl, news)
@@ -175,10 +181,38 @@ def test_prefill_full_size(name):
     torch.cuda.synchronize()
     got = out.cpu()
     del d, out
-    subset = G.sample_rows(rows, 40)
+    return wl, rows, kc, vc, got
+
+
+def test_prefill_full_size_every_row_p2():
+    """Every row and head of the 70B-shaped chunk (4 x 1024 rows x 64 heads)
+    against the oracle."""
+    wl, rows, kc, vc, got = _full_prefill("p2")
+    ref = G.oracle_prefill(wl, kc, vc, rows)
+    atol, rtol = G.tol_for(wl)
+    _err_report(got, ref, atol, rtol, "prefill full p2 (every row)")
+    G.assert_close(got, ref, atol, rtol, what="prefill full p2")
+
+
+def test_prefill_full_size_p1_whole_sequences_and_tile_edges():
+    """The 7B-shaped prompts (8 x 2048 rows): every row of the first and the
+    last sequence, and in every other sequence the first, second and last
+    row of each 256-row tile and the rows on each side of its 64-key KV
+    tile boundaries."""
+    wl, rows, kc, vc, got = _full_prefill("p1")
+    qsl = rows.query_start_loc
+    pick = set(range(int(qsl[0]), int(qsl[1]))) | set(range(int(qsl[-2]), int(qsl[-1])))
+    for b in range(1, len(qsl) - 2):
+        r0, n = int(qsl[b]), int(qsl[b + 1] - qsl[b])
+        for t0 in range(0, n, 256):
+            for off in (0, 1, 63, 64, 127, 128, 191, 192, 255):
+                if t0 + off < n:
+                    pick.add(r0 + t0 + off)
+    subset = sorted(pick)
     ref = G.oracle_prefill(wl, kc, vc, rows, subset)
     atol, rtol = G.tol_for(wl)
-    G.assert_close(got[subset], ref[subset], atol, rtol, what=f"prefill full {name}")
+    _err_report(got[subset], ref[subset], atol, rtol, f"prefill full p1 ({len(subset)} rows)")
+    G.assert_close(got[subset], ref[subset], atol, rtol, what="prefill full p1")
 
 
 # --- bf16 query and K/V: the f16 P x V path and its bf16 redo ------------------
@@ -284,3 +318,32 @@ def test_prefill_bf16_f16_range_boundary(value, flagged):
     assert bool((ws > 0).any()) == flagged
     atol, rtol = G.tol_for(wl)
     G.assert_close(out, ref, atol, rtol, what=f"prefill bf16 boundary {value}")
+
+
+def test_prefill_bf16_tiny_values_on_the_f16_path():
+    """V scaled by 1e-6: bf16 values below 2^-14 are staged as f16
+    subnormals (spacing 2^-24).  No workgroup is flagged (nothing reaches
+    2^16), and every output is within 2^-25 plus 1e-2 relative of the
+    oracle, the bound that rounding states: each staged value is off by
+    at most 2^-25, and an output is a weighted mean of the values."""
+    base, lens, news = SMALL["gqa_bf16"]
+    cfg = shrink(base, batch=len(lens), lengths=("list", lens), pool_blocks=0)
+    wl = make_workload(cfg, seed=209)
+    wl = type(wl)(**{**wl.__dict__, "tok_value": (wl.tok_value.float() * 1e-6).to(torch.bfloat16)})
+    rows = make_prefill_rows(wl, news, seed=210)
+    G.say("prefill bf16 tiny values")
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_prefill(wl, kc, vc, rows)
+    d = G.to_device(wl)
+    ws = _ws(wl, rows)
+    c = wl.cfg
+    q = rows.query.to("cuda")
+    qsl = torch.from_numpy(rows.query_start_loc).to("cuda")
+    out = torch.empty_like(q)
+    pa.prefill(out, q, d.kc, d.vc, d.tables, d.lens, qsl, rows.max_query_len, wl.scale,
+               c.block_size, c.num_kv_heads, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.max()) == 0
+    # 2^-25 from the staged values, plus the output's own bf16 rounding and
+    # the weights' f16 rounding, both relative
+    G.assert_close(out, ref, 2.0 ** -25, 1e-2, what="prefill bf16 tiny values")

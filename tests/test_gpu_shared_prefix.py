@@ -1,8 +1,9 @@
 """Shared-prefix decode on the GPU (pa_decode_shared_prefix through the C
 ABI) against the fp64 decode oracle: the result must be plain decode's, for
 sequences shorter than, equal to and longer than the shared prefix, empty
-ones included, across the dtype / group / block-size / head_dim variants and
-at the full mixed-length fp8 workload size (sampled rows)."""
+ones included, across the dtype / group / block-size / head_dim variants,
+and every element at the full workload sizes, whose batches are built
+through the host allocator, block manager and prefix cache."""
 
 import numpy as np
 import pytest
@@ -78,17 +79,43 @@ def test_shared_prefix_deterministic():
 
 
 @pytest.mark.parametrize("name", ["c5", "c6"])
-def test_shared_prefix_full_size(name):
+def test_prefix_cache_chain_full_size(name):
+    """The full-size shared-prompt batch built through the host chain
+    (allocator with the seeded order -> prompt admitted and cached ->
+    every request admitted through the prefix cache -> prompt sequence
+    released), its K/V written at the chain's slots by pa_reshape_and_cache,
+    then pa_decode and pa_decode_shared_prefix: every output element of
+    both against the decode oracle on the same tables and caches.  Prompt
+    blocks carry one reference per request that fills them plus the
+    cache's; releasing every request and evicting the cache frees the
+    whole pool."""
     cfg = get_config(name)
     wl = make_workload(cfg)
     P = cfg.shared_prefix_tokens
-    G.say(f"shared prefix full {name}: B={cfg.batch} P={P}")
-    kc, vc = G.oracle_caches(wl)
-    d = G.to_device(wl)
-    out = _run(wl, P, d)
+    bs = cfg.block_size
+    ch = G.admit_chain(wl)
+    G.say(f"prefix-cache chain full {name}: B={cfg.batch} P={P} writes={len(ch.slots)}")
+    fills = np.array([min(int(L), P) // bs for L in ch.batch.seq_lens])
+    for j, blk in enumerate(ch.batch.prompt_blocks):
+        assert ch.alloc.refcount(int(blk)) == 1 + int((fills > j).sum())
+    kc, vc = G.chain_oracle_caches(wl, ch)
+    d = G.chain_to_device(wl, ch)
+    plain = G.gpu_decode(wl, d)
+    shared = torch.empty_like(d.query)
+    pb = torch.from_numpy(ch.batch.prompt_blocks.astype(np.int32)).to(d.kc.device)
+    pa.decode_shared_prefix(shared, d.query, d.kc, d.vc, d.tables, d.lens, pb, P, wl.scale,
+                            bs, cfg.num_kv_heads, k_scale=wl.k_scale, v_scale=wl.v_scale,
+                            kv_dtype="fp8" if cfg.kv_dtype == "fp8" else None)
     torch.cuda.synchronize()
-    got = out.cpu()
-    pairs = G.sample_pairs(wl, 48)
-    ref = G.oracle_decode(wl, kc, vc, pairs)
+    assert G.caches_equal(d.kc, kc) and G.caches_equal(d.vc, vc)
+    del d
+    ref = G.chain_oracle_decode(wl, ch, kc, vc)
     atol, rtol = G.tol_for(wl)
-    G.assert_close(got, ref, atol, rtol, pairs=pairs, what=f"shared prefix full {name}")
+    G.err_summary(plain, ref, atol, rtol, f"chain {name} pa_decode")
+    G.err_summary(shared, ref, atol, rtol, f"chain {name} pa_decode_shared_prefix")
+    G.assert_close(plain, ref, atol, rtol, what=f"chain {name} pa_decode")
+    G.assert_close(shared, ref, atol, rtol, what=f"chain {name} pa_decode_shared_prefix")
+    for sid in ch.batch.seq_ids:
+        ch.manager.free_sequence(sid)
+    ch.cache.evict(wl.num_blocks)
+    assert ch.cache.size() == 0 and ch.alloc.num_free() == wl.num_blocks
