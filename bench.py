@@ -6,6 +6,10 @@ new K/V token into its cache slot (pa_reshape_and_cache), then single-query
 attention of every query head over its sequence's paged K/V
 (pa_decode: partition kernel, plus the merge kernel when the plan splits).
 Inputs are synthetic and seeded (synth/), resident in HBM before timing.
+By default the headline is the 70B-shaped GQA decode (64 sequences of 4096
+tokens, 1 GiB of KV per call), with the 7B-shaped decode under "also".
+Batches whose sequences share a prompt take their block tables from the
+host allocator and prefix cache.
 
 Like the layers of a model, consecutive steps use different copies of the
 KV pool (enough copies that together they are several times the 256 MB
@@ -18,7 +22,8 @@ Prints ONE JSON line:
   roofline        the decode call measured with HIP events (created without
                   the system-scope fence, so recording them does not flush
                   the caches between the timed launches) on the launch
-                  stream: algorithmic KV bytes per launch / mean duration,
+                  stream, --timed-launches calls after the timed steps:
+                  algorithmic KV bytes per launch / mean duration,
                   against the 8 TB/s HBM peak; `traffic` from the committed
                   rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it was taken
                   from the current kernel source, else null
@@ -129,6 +134,20 @@ class HipTimingEvents:
         self.events = []
 
 
+def host_threads() -> dict:
+    """The host cores this process may run on, and the threads the oracle's
+    BLAS and torch's CPU ops use on them."""
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        pass
+    import torch
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": blas,
+            "torch_threads": torch.get_num_threads()}
+
+
 def cpu_baseline(wl, seconds: float):
     """The oracle, unchanged, over the sequences of the batch in order (from
     the first again after the last) until the time budget is spent."""
@@ -155,18 +174,10 @@ def cpu_baseline(wl, seconds: float):
         kv_bytes += int(wl.seq_lens[b]) * c.num_kv_heads * c.head_dim * 2 * esz
         if t_used >= seconds:
             break
-    threads = 1
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        pass
-    import torch
-    threads = max(threads, torch.get_num_threads())
     return {
         "value": round(kv_bytes / t_used / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        **host_threads(),
         "kind": "oracle",
         "sample": f"fp64 oracle decode of {done} sequences ({done / c.batch:.1f} passes over the "
                   f"batch of {c.batch}, all {c.num_q_heads} query heads, {kv_bytes / 1e6:.1f} MB "
@@ -306,7 +317,7 @@ def cpu_baseline_prefill(wl, rows, seconds: float):
     return {
         "value": round(flops / used / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(torch.get_num_threads()),
+        **host_threads(),
         "kind": "oracle",
         "sample": f"fp64 prefill oracle on {len(sel)} evenly spaced rows of sequence 0 "
                   f"({n0} rows, {L0} tokens), all {c.num_q_heads} query heads, "
@@ -461,55 +472,46 @@ def bench_prefill(args) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", help="workload name or c1..c5 (default: the 7B-shaped decode)")
-    ap.add_argument("--partition-tokens", type=int, default=0)
-    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
-    ap.add_argument("--layers", type=int, default=0,
-                    help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
-    ap.add_argument("--hot-iters", type=int, default=20)
-    ap.add_argument("--write-iters", type=int, default=20,
-                    help="pa_reshape_and_cache launches timed on their own, after the steps")
-    ap.add_argument("--shared-prefix", action="store_true",
-                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
-    ap.add_argument("--time-every", type=int, default=4,
-                    help="event-time the attention launch of every N-th timed step")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--max-query-len", type=int, default=0,
-                    help="prefill: max_query_len passed to pa_prefill (sizes its grid; 0 = the true maximum)")
-    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "swap"],
-                    help="decode: the decode hot path (default); prefill: causal prefill of "
-                         "new tokens over the cache (--config p1 | p2); swap: the batch's KV "
-                         "blocks swapped out to pinned host memory and back in (pa_swap_blocks)")
-    args = ap.parse_args()
+def chain_tables(wl):
+    """A shared-prompt workload's tables and K/V slots built through the
+    host chain (the library's allocator handing out ids in the workload's
+    seeded order, the prompt admitted and cached, every request admitted
+    through the prefix cache, the prompt's own sequence released).  They
+    must equal the seeded layout; returns (tables, seq_lens, slots, rows,
+    prompt_blocks)."""
+    import numpy as np
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the decode path shards by kv head or by sequence with no exchange inside attention, "
-              "and the library has no multi-GPU launch to measure.", file=sys.stderr)
-        return 2
+    import paged_kv_cache_462_amd as pa
 
+    c = wl.cfg
+    alloc = pa.BlockAllocator(wl.num_blocks, wl.pool_order[::-1])
+    mgr = pa.BlockManager(alloc, c.block_size)
+    cache = pa.PrefixCache(alloc, c.block_size)
+    P = c.shared_prefix_tokens
+    prompt = wl.token_ids[int(np.argmax(wl.seq_lens))][:P]
+    batch = pa.admit_with_shared_prompt(mgr, cache, prompt, wl.token_ids, wl.max_blocks)
+    if not (np.array_equal(batch.tables, wl.block_tables)
+            and np.array_equal(batch.seq_lens, wl.seq_lens)):
+        raise SystemExit("the host chain's tables differ from the seeded layout")
+    slots, rows = [], []
+    for i, first, sl in batch.writes:
+        pos = np.arange(first, first + len(sl))
+        rows.append(pos if i < 0 else wl.position_rows(i, pos))
+        slots.append(sl)
+    return (batch.tables, batch.seq_lens, np.concatenate(slots), np.concatenate(rows),
+            batch.prompt_blocks)
+
+
+def run_decode(name: str, args, cpu_seconds: float) -> dict:
+    """One decode workload: the timed steps, the event-timed launches, the
+    cache-write timings and (cpu_seconds > 0) the oracle on the host."""
     import numpy as np
     import torch
 
     import paged_kv_cache_462_amd as pa
     from synth import get_config, make_workload
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    pa.load()
-    if args.op == "swap":
-        return bench_swap(args)
-    if args.op == "prefill":
-        return bench_prefill(args)
-    cfg = get_config(args.config)
+    cfg = get_config(name)
     log(f"[bench] generating {cfg.name}")
     wl = make_workload(cfg)
     dev = torch.device("cuda:0")
@@ -521,12 +523,22 @@ def main() -> int:
     kc = torch.zeros(shape, dtype=st, device=dev)
     vc = torch.zeros(shape, dtype=st, device=dev)
     q = wl.query.to(dev)
-    tables = torch.from_numpy(wl.block_tables).to(dev)
-    lens = torch.from_numpy(wl.seq_lens).to(dev)
+    source = "seeded layout"
+    if c.shared_prefix_tokens:
+        # shared-prompt batches come out of the allocator and prefix cache
+        tab_np, lens_np, slots_np, rows_np, prompt_blocks_np = chain_tables(wl)
+        ri = torch.from_numpy(rows_np)
+        fill_k, fill_v = wl.tok_key[ri], wl.tok_value[ri]
+        source = "host allocator + prefix cache"
+    else:
+        tab_np, lens_np, slots_np = wl.block_tables, wl.seq_lens, wl.slot_mapping
+        fill_k, fill_v = wl.tok_key, wl.tok_value
+        prompt_blocks_np = wl.shared_blocks
+    tables = torch.from_numpy(tab_np).to(dev)
+    lens = torch.from_numpy(lens_np).to(dev)
     # fill the cache once (set-up, untimed)
-    pa.reshape_and_cache(wl.tok_key.to(dev), wl.tok_value.to(dev),
-                         torch.from_numpy(wl.slot_mapping).to(dev), kc, vc,
-                         k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
+    pa.reshape_and_cache(fill_k.to(dev), fill_v.to(dev), torch.from_numpy(slots_np).to(dev),
+                         kc, vc, k_scale=wl.k_scale, v_scale=wl.v_scale, kv_dtype=kvd)
     pool_bytes = 2 * kc.numel() * kc.element_size()
     n_layers = args.layers or max(1, -(-(3 << 30) // pool_bytes))
     layers = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(n_layers - 1)]
@@ -547,7 +559,7 @@ def main() -> int:
         ws_bytes = pa.decode_shared_prefix_workspace_bytes(
             c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, wl.max_blocks,
             c.shared_prefix_tokens)
-        prefix_blocks = torch.from_numpy(wl.shared_blocks.astype(np.int32)).to(dev)
+        prefix_blocks = torch.from_numpy(prompt_blocks_np.astype(np.int32)).to(dev)
     else:
         ws_bytes = pa.decode_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads, c.head_dim,
                                              c.block_size, wl.max_blocks, args.partition_tokens)
@@ -582,27 +594,31 @@ def main() -> int:
         decode(i % n_layers)
     torch.cuda.synchronize()
 
+    # the timed steps: nothing but the steps between the two synchronisations
     K = args.steps
-    timer = HipTimingEvents()
-    # every time_every-th step brackets its decode call with timing events
-    # (each marker idles the GPU for a few microseconds)
-    sampled = list(range(0, K, max(1, args.time_every)))
-    evs = {i: (timer.create(), timer.create()) for i in sampled}
-    log(f"[bench] timing {K} steps ({len(sampled)} decode launches event-timed)")
-    torch.cuda.synchronize()
+    log(f"[bench] timing {K} steps")
     t0 = time.perf_counter()
     for i in range(K):
         write(i % n_layers)
-        ev = evs.get(i)
-        if ev:
-            timer.record(ev[0], stream)
         decode(i % n_layers)
-        if ev:
-            timer.record(ev[1], stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
-    dec_ms = [timer.elapsed_ms(a, b) for a, b in evs.values()]
+
+    # then the same steps again with the decode call of each between two
+    # HIP events on its stream (each marker idles the GPU for a few
+    # microseconds, so these steps are not the timed ones)
+    timer = HipTimingEvents()
+    n_ev = max(args.timed_launches, 1)
+    evs = [(timer.create(), timer.create()) for _ in range(n_ev)]
+    log(f"[bench] {n_ev} decode launches event-timed")
+    for i, (a, b) in enumerate(evs):
+        write(i % n_layers)
+        timer.record(a, stream)
+        decode(i % n_layers)
+        timer.record(b, stream)
+    torch.cuda.synchronize()
+    dec_ms = [timer.elapsed_ms(a, b) for a, b in evs]
     dec_mean = float(np.mean(dec_ms))
     dec_med = float(np.median(dec_ms))
 
@@ -657,6 +673,8 @@ def main() -> int:
             "bulk_GBps": round(wl.num_tokens * tok_bytes / (bulk_ms * 1e-3) / 1e9, 1),
             "bytes_per_token": tok_bytes,
         }
+    del layers, kc, vc, ws
+    torch.cuda.empty_cache()
 
     kv_unique = wl.unique_kv_bytes()
     kv_logical = wl.logical_kv_bytes()
@@ -708,6 +726,7 @@ def main() -> int:
             "schedule": plan["schedule"],
             "partition_tokens": plan["partition_tokens"],
             "path": {0: "auto", 1: "valu", 2: "mfma"}[args.path],
+            "block_tables": source,
             "kv_bytes_unique": kv_unique,
             "kv_bytes_logical": kv_logical,
             "parallelism": "single GPU",
@@ -718,9 +737,83 @@ def main() -> int:
         "cache_write": cache_write,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (~{args.cpu_seconds}s)")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    if cpu_seconds > 0:
+        log(f"[bench] cpu baseline (~{cpu_seconds}s)")
+        res["cpu_baseline"] = cpu_baseline(wl, cpu_seconds)
+    return res
+
+
+# The 70B-shaped GQA decode is the largest single-GPU configuration (1 GiB of
+# KV per call) and the headline; the 7B-shaped one rides along.
+HEADLINE = "c3"
+ALSO = ("c2",)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default=None,
+                    help="workload name or c1..c6; default: the 70B-shaped GQA decode as the "
+                         "headline, with the 7B-shaped decode alongside")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--path", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="KV pool copies the steps rotate through (0: enough for >= 3 GiB)")
+    ap.add_argument("--hot-iters", type=int, default=20)
+    ap.add_argument("--write-iters", type=int, default=20,
+                    help="pa_reshape_and_cache launches timed on their own, after the steps")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode through pa_decode_shared_prefix (workloads with a shared prefix)")
+    ap.add_argument("--timed-launches", type=int, default=40,
+                    help="decode launches timed one by one with HIP events, after the timed steps")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="prefill: event-time the attention launch of every N-th timed step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--max-query-len", type=int, default=0,
+                    help="prefill: max_query_len passed to pa_prefill (sizes its grid; 0 = the true maximum)")
+    ap.add_argument("--op", default="decode", choices=["decode", "prefill", "swap"],
+                    help="decode: the decode hot path (default); prefill: causal prefill of "
+                         "new tokens over the cache (--config p1 | p2); swap: the batch's KV "
+                         "blocks swapped out to pinned host memory and back in (pa_swap_blocks)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the decode path shards by kv head or by sequence with no exchange inside attention, "
+              "and the library has no multi-GPU launch to measure.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_cache_462_amd as pa
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pa.load()
+    if args.op == "swap":
+        if args.config is None:
+            args.config = "c2"
+        return bench_swap(args)
+    if args.op == "prefill":
+        if args.config is None:
+            args.config = "p1"
+        return bench_prefill(args)
+    cpu_s = 0.0 if args.no_cpu_baseline else args.cpu_seconds
+    if args.config is not None:
+        print(json.dumps(run_decode(args.config, args, cpu_s)), flush=True)
+        return 0
+    res = run_decode(HEADLINE, args, cpu_s)
+    res["also"] = {}
+    for name in ALSO:
+        r = run_decode(name, args, 0.0)
+        res["also"][r["config"]["workload"]] = {
+            k: r[k] for k in ("value", "unit", "ms_per_step", "pct_of_hbm_peak", "tokens_per_s",
+                              "dtype", "config", "roofline", "cache_write")}
     print(json.dumps(res), flush=True)
     return 0
 

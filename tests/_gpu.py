@@ -268,8 +268,17 @@ def chain_oracle_decode(wl: Workload, ch: Chain, kc, vc) -> np.ndarray:
                                   wl.cfg.block_size)
 
 
-def err_summary(got: torch.Tensor, ref: np.ndarray, atol: float, rtol: float, what: str) -> None:
-    g = got.detach().to("cpu", torch.float64).numpy()
+# error summaries of the full-size checks, printed at the end of the session
+# (tests/conftest.py) so that they show however pytest captures output
+SUMMARY: List[str] = []
+
+
+def err_summary(got, ref: np.ndarray, atol: float, rtol: float, what: str) -> None:
+    g = got.detach().to("cpu", torch.float64).numpy() if isinstance(got, torch.Tensor) else got
     err = np.abs(g - ref)
-    say(f"{what}: {err.size} outputs, max abs err {err.max():.2e}, max err / bound "
-        f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")
+    big = np.abs(ref) > 1e-2
+    rel = f"{(err[big] / np.abs(ref[big])).max():.2e}" if big.any() else "-"
+    line = (f"{what}: {err.size} outputs, max abs err {err.max():.2e}, max rel err "
+            f"(|ref| > 0.01) {rel}, max err / bound {(err / (atol + rtol * np.abs(ref))).max():.3f}")
+    SUMMARY.append(line)
+    say(line)

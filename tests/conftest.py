@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # the full-size parity checks' error summaries (max error against the
+    # tolerance bound), when GPU tests ran in this session
+    g = sys.modules.get("tests._gpu")
+    lines = getattr(g, "SUMMARY", None)
+    if lines:
+        terminalreporter.write_sep("-", "parity error summaries")
+        for line in lines:
+            terminalreporter.write_line(line)

@@ -299,12 +299,7 @@ def test_full_size(name):
     del d
     ref = G.oracle_decode(wl, kc, vc)
     atol, rtol = G.tol_for(wl)
-    g = out.to("cpu", torch.float64).numpy()
-    err = np.abs(g - ref)
-    big = np.abs(ref) > 1e-2
-    G.say(f"full {name}: {err.size} outputs, max abs err {err.max():.2e}, max rel err "
-          f"(|ref| > 0.01) {(err[big] / np.abs(ref[big])).max():.2e}, max err / bound "
-          f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")
+    G.err_summary(out, ref, atol, rtol, f"decode full {name}")
     G.assert_close(out, ref, atol, rtol, what=f"full {name}")
 
 

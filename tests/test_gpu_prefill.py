@@ -163,13 +163,6 @@ def test_prefill_after_gpu_cache_write_of_the_chunk():
     G.assert_close(out, ref, atol, rtol, what="prefill after chunk write")
 
 
-def _err_report(got, ref, atol, rtol, what):
-    g = got.to(torch.float64).numpy() if isinstance(got, torch.Tensor) else got
-    err = np.abs(g - ref)
-    G.say(f"{what}: {err.size} outputs, max abs err {err.max():.2e}, max err / bound "
-          f"{(err / (atol + rtol * np.abs(ref))).max():.3f}")
-
-
 def _full_prefill(name):
     cfg, news = get_prefill_config(name)
     wl = make_workload(cfg)
@@ -190,7 +183,7 @@ def test_prefill_full_size_every_row_p2():
     wl, rows, kc, vc, got = _full_prefill("p2")
     ref = G.oracle_prefill(wl, kc, vc, rows)
     atol, rtol = G.tol_for(wl)
-    _err_report(got, ref, atol, rtol, "prefill full p2 (every row)")
+    G.err_summary(got, ref, atol, rtol, "prefill full p2 (every row)")
     G.assert_close(got, ref, atol, rtol, what="prefill full p2")
 
 
@@ -211,7 +204,7 @@ def test_prefill_full_size_p1_whole_sequences_and_tile_edges():
     subset = sorted(pick)
     ref = G.oracle_prefill(wl, kc, vc, rows, subset)
     atol, rtol = G.tol_for(wl)
-    _err_report(got[subset], ref[subset], atol, rtol, f"prefill full p1 ({len(subset)} rows)")
+    G.err_summary(got[subset], ref[subset], atol, rtol, f"prefill full p1 ({len(subset)} rows)")
     G.assert_close(got[subset], ref[subset], atol, rtol, what="prefill full p1")
 
 
