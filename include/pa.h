@@ -169,6 +169,32 @@ int pa_decode(pa_tensor* out, const pa_tensor* query,
               const pa_launch* launch);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and launches
+ * as pa_decode, but a split plan's (max, sum, partial output) triples and
+ * merge plan go to a fixed device array the library holds (16 MiB per GPU
+ * it runs on, kept until the process ends) instead of a caller workspace:
+ *   launch   stream, partition_tokens, path and error_flags as for
+ *            pa_decode; workspace must be NULL with workspace_bytes 0
+ *            (PA_ERR_INVALID_ARG otherwise)
+ * A plan whose triples do not fit returns PA_ERR_WORKSPACE before any
+ * launch (the balanced plan needs (shares + B) * Hq * (D + 2) * 4 + 8 B
+ * bytes, shares = 256, or 768 for an fp8 cache on the matrix cores: e.g.
+ * 10.7 MB for B = 64, Hq = 64, D = 128).  Nothing in the array needs to
+ * start cleared: the decode launch writes every entry the merge reads.
+ * The first call on a device looks the array's address up (no allocation);
+ * later calls reuse it.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (other streams, other host threads) race:
+ * serialise them.
+ */
+int pa_decode_noalloc(pa_tensor* out, const pa_tensor* query,
+                      const pa_tensor* key_cache, const pa_tensor* value_cache,
+                      const pa_tensor* block_tables, const pa_tensor* seq_lens,
+                      float scale, int32_t block_size, int32_t num_kv_heads,
+                      const pa_launch* launch);
+
+/*
  * pa_prefill -- causal attention of a batch of new tokens over the paged
  * cache ("5.KV Cache 管理 & PagedAttention", question 6, `MHAWithCache`
  * prefill branch, lower-triangular mask; question 19, query tiles against

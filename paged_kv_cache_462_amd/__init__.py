@@ -28,6 +28,7 @@ from .ops import (  # noqa: F401
     build_info,
     copy_blocks,
     decode,
+    decode_noalloc,
     decode_plan,
     decode_shared_prefix,
     decode_shared_prefix_workspace_bytes,

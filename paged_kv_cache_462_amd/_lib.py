@@ -63,6 +63,7 @@ _P = c_void_p  # pa_prefix_cache*
 SIGNATURES = {
     "pa_reshape_and_cache": (c_int32, [_T, _T, _T, _T, _T, _L]),
     "pa_decode": (c_int32, [_T, _T, _T, _T, _T, _T, c_float, c_int32, c_int32, _L]),
+    "pa_decode_noalloc": (c_int32, [_T, _T, _T, _T, _T, _T, c_float, c_int32, c_int32, _L]),
     "pa_prefill": (c_int32, [_T, _T, _T, _T, _T, _T, _T, c_int32, c_float, c_int32, c_int32, _L]),
     "pa_decode_shared_prefix": (c_int32, [_T, _T, _T, _T, _T, _T, _T, c_int32, c_float, c_int32,
                                           c_int32, _L]),

@@ -180,7 +180,12 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
                  const pa_tensor* seq_lens, float scale, int32_t block_size,
                  int32_t num_kv_heads, const pa_launch* launch, int64_t extra_ws_bytes,
                  pa::DecodeParams* out_p, pa::DecodeVariant* out_v, Plan* out_plan, bool* empty,
-                 bool balanced_only = false) {
+                 bool balanced_only = false, int64_t scratch_cap = -1,
+                 int64_t* out_slots = nullptr) {
+  // scratch_cap >= 0: the triples go to the library's own scratch of that
+  // many bytes instead of the caller's workspace (the launch must carry
+  // none); the layout is the one below with slots = the shares the launch
+  // deals plus B, and the pointers are left for the caller to set
   *empty = false;
   int rc;
   if ((rc = check_tensor(query, "query", 3)) || (rc = check_tensor(out, "out", 3)) ||
@@ -245,7 +250,7 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   }
   v.gt = v.path == 2 ? 16 : (G == 1 ? 1 : (G == 2 ? 2 : 4));
   if (!pa::decode_variant_built(v)) return fail(PA_ERR_UNSUPPORTED, "no decode variant for this dtype / head_dim");
-  if (plan.split) {
+  if (plan.split && scratch_cap < 0) {
     const int64_t need = plan.ws_bytes + extra_ws_bytes;
     if (!launch || !launch->workspace || launch->workspace_bytes < (size_t)need)
       return fail(PA_ERR_WORKSPACE, "split decode needs %lld workspace bytes", (long long)need);
@@ -297,7 +302,19 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
-  if (plan.split) {
+  // a balanced piece of sequence b sits at slot (its share) + b
+  const int64_t slots = scratch_cap >= 0 && plan.sched == pa::kSchedBalanced
+                            ? (int64_t)p.nwc + B : plan.slots;
+  if (plan.split && scratch_cap >= 0) {
+    const int64_t need = slots * Hq * (D + 2) * (int64_t)sizeof(float) +
+                         (plan.sched == pa::kSchedBalanced ? B * 2 * (int64_t)sizeof(int32_t) : 0);
+    if (need > scratch_cap)
+      return fail(PA_ERR_WORKSPACE,
+                  "this plan needs %lld bytes of scratch; the library holds %lld (use pa_decode "
+                  "with a workspace)", (long long)need, (long long)scratch_cap);
+  }
+  if (out_slots) *out_slots = slots;
+  if (plan.split && scratch_cap < 0) {
     p.ws_acc = static_cast<float*>(launch->workspace);
     p.ws_ml = p.ws_acc + plan.slots * Hq * D;
     p.ws_meta = reinterpret_cast<int32_t*>(p.ws_ml + plan.slots * Hq * 2);
@@ -381,6 +398,36 @@ int pa_decode(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache
                         block_size, num_kv_heads, launch, 0, &p, &v, &plan, &empty);
   if (rc || empty) return rc;
   hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  hipError_t e = pa::launch_decode(p, v, stream);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_decode_noalloc(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_cache,
+                      const pa_tensor* value_cache, const pa_tensor* block_tables,
+                      const pa_tensor* seq_lens, float scale, int32_t block_size,
+                      int32_t num_kv_heads, const pa_launch* launch) {
+  if (launch && (launch->workspace || launch->workspace_bytes))
+    return fail(PA_ERR_INVALID_ARG, "pa_decode_noalloc takes no workspace (it uses the library's own)");
+  pa::DecodeParams p;
+  pa::DecodeVariant v;
+  Plan plan;
+  bool empty;
+  int64_t slots = 0;
+  int rc = decode_setup(out, query, key_cache, value_cache, block_tables, seq_lens, scale,
+                        block_size, num_kv_heads, launch, 0, &p, &v, &plan, &empty, false,
+                        pa::kDecodeScratchBytes, &slots);
+  if (rc || empty) return rc;
+  hipStream_t stream = launch ? static_cast<hipStream_t>(launch->stream) : nullptr;
+  if (plan.split) {
+    void* base = nullptr;
+    hipError_t e = pa::decode_scratch(stream, &base);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "scratch lookup failed: %s", hipGetErrorString(e));
+    const int64_t Hq = p.Hq, D = p.D;
+    p.ws_acc = static_cast<float*>(base);
+    p.ws_ml = p.ws_acc + slots * Hq * D;
+    p.ws_meta = reinterpret_cast<int32_t*>(p.ws_ml + slots * Hq * 2);
+  }
   hipError_t e = pa::launch_decode(p, v, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return PA_OK;

@@ -57,10 +57,18 @@
 // read with v_readlane, so every K/V address is a scalar 64-bit block base
 // plus a 32-bit per-lane offset; the next tile's loads are issued before the
 // current tile is computed.
+#include <mutex>
 #include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
+
+// The library's own decode scratch (pa_decode_noalloc): triples and the
+// merge plan of one call, for callers that cannot allocate.  Every GPU the
+// library runs on holds one copy until the process ends.  In host code
+// this name stands for the array, not for its device address: the address
+// is looked up per device below and only that is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[pa::kDecodeScratchBytes];
 
 namespace pa {
 
@@ -1143,6 +1151,37 @@ void decode_launch_shape(const DecodeVariant& v, int* max_waves, int* workgroups
   const bool fp8_mfma = v.path == 2 && v.kvkind == K_FP8;
   *max_waves = fp8_mfma ? kFp8Waves : kMaxWaves;
   *workgroups = fp8_mfma ? kBalancedWorkgroupsFp8 : kBalancedWorkgroups;
+}
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // first use on this device: its address, with that device current
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeParams& p, const DecodeVariant& v, hipStream_t stream) {

@@ -79,6 +79,13 @@ struct DecodeVariant {
   int gt;      // query heads per workgroup tile (MFMA: 16; VALU: 1, 2 or 4)
 };
 
+// Device scratch the library keeps for pa_decode_noalloc: one fixed array
+// per device (a file-scope __device__ array in pa_decode.hip), found once per
+// device.  decode_scratch gives its address on the device of `stream` (the
+// current device for the null stream); no allocation is made.
+constexpr int64_t kDecodeScratchBytes = 16ll << 20;
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 // Launch the decode (and the merge when p.split).  Returns hipSuccess or the
 // launch error; hipErrorNotSupported when no variant matches.
 hipError_t launch_decode(const DecodeParams& p, const DecodeVariant& v,

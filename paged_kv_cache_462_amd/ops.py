@@ -149,6 +149,23 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
                            int(block_size), int(num_kv_heads), byref(ln)))
 
 
+def decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                   scale: float, block_size: int, num_kv_heads: int,
+                   k_scale: float = 1.0, v_scale: float = 1.0, kv_dtype: Optional[str] = None,
+                   partition_tokens: int = 0, path: int = PATH_AUTO,
+                   stream: Optional[torch.cuda.Stream] = None,
+                   error_flags: Optional[torch.Tensor] = None) -> None:
+    """pa_decode_noalloc: pa_decode with the library's own fixed device
+    scratch; nothing is allocated, here or in the library."""
+    fp8 = _is_fp8(key_cache, kv_dtype)
+    args = (_desc(out), _desc(query), _desc(key_cache, fp8, k_scale),
+            _desc(value_cache, fp8, v_scale), _desc(block_tables), _desc(seq_lens))
+    ln = _launch(query, None, partition_tokens, path, stream, error_flags)
+    check(load().pa_decode_noalloc(*(byref(a) for a in args), ctypes.c_float(scale),
+                                   int(block_size), int(num_kv_heads), byref(ln)))
+
+
 def decode_shared_prefix_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int,
                                          head_dim: int, block_size: int, max_blocks: int,
                                          prefix_tokens: int) -> int:
