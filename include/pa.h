@@ -266,12 +266,14 @@ int64_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t n
  * through the block tables ("5.KV Cache 管理 & PagedAttention", question 20;
  * "KV Cache 优化与内存管理深度解析：PagedAttention 原理与实践",
  * `HashBasedCaching`).  The result is pa_decode's.  The prefix part of the
- * attention is taken once for the whole batch -- every query row of a kv
- * head against the prefix keys, as one dense product on the matrix cores,
- * each row limited to its sequence's length -- instead of once per
- * sequence; the rest of every sequence goes through the decode kernels,
- * and the merge kernel folds both partial results (the pages' rescale
- * identity across pieces).
+ * attention is taken for all (sequence, query head) rows of a kv head at
+ * once, each row limited to its sequence's length, instead of once per
+ * sequence: with rows = batch * (num_q_heads / num_kv_heads) below 1024,
+ * inside the matrix-core decode launch in groups of 16 rows (the kernel's
+ * query columns), from 1024 rows on as a separate launch of the prefill
+ * kernel in 256-row tiles.  The rest of every sequence goes through the
+ * decode kernel, and the merge kernel folds the partial results (the
+ * pages' rescale identity across pieces).
  *   out, query, key_cache, value_cache, block_tables, seq_lens, scale,
  *   block_size, num_kv_heads: as for pa_decode, with an f16 or bf16 query
  *                 and a positive scale
@@ -282,11 +284,12 @@ int64_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t n
  *                 pa_decode_shared_prefix_workspace_bytes); partition_tokens
  *                 must be 0 (the plan is always the balanced schedule, so
  *                 the batch is at most 2048 sequences)
- * Supported head_dim: 64, 128.  Three launches (prefix pass, decode of the
- * rest, merge), deterministic.  It pays when the prefix is most of most
- * sequences; when many sequences end inside the prefix, the prefix pass and
- * the merge of its pieces cost more than they save and pa_decode is the
- * faster call.  The lengths stay on the device, so the caller chooses.
+ * Below 1024 rows per kv head the decode runs on the matrix-core path (a
+ * launch asking for the VALU path is refused).  Supported head_dim: 64,
+ * 128.  Two launches (decode with the grouped prefix work, merge) or three
+ * (prefix pass, decode of the rest, merge), deterministic.  Whether it is
+ * faster than pa_decode depends on how much of the batch the prefix is;
+ * the lengths stay on the device, so the caller chooses.
  */
 int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query,
                             const pa_tensor* key_cache, const pa_tensor* value_cache,

@@ -299,6 +299,11 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
+#ifdef PA_EXP_COST_TOKENS
+  p.cost_tokens = PA_EXP_COST_TOKENS;
+  p.cost_lo = PA_EXP_COST_LO;
+  p.cost_hi = PA_EXP_COST_HI;
+#endif
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
@@ -325,25 +330,49 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   return PA_OK;
 }
 
-// How the shared-prefix pass splits its work: 256-row tiles of the batch's
-// (sequence, query head) rows per kv head, and the prefix keys in pieces of
-// a multiple of 64 keys, enough pieces to give the GPU
-// about 256 workgroups.
+// How the shared-prefix decode takes its prefix part.  Each kv head's
+// prefix keys serve rows = B * G (sequence, query head) rows.
+// - Grouped (rows < kPassRows): inside the matrix-core decode launch, the
+//   rows in groups of 16 (one wave each, the kernel's query columns) over
+//   pieces of about kGroupTokens keys, so a wave's piece is about as many
+//   tiles as a decode share; every group reads the prefix tiles it needs
+//   again (from the caches).
+// - Pass (rows >= kPassRows): a launch of the prefill kernel before the
+//   decode, 256-row tiles of the rows against pieces of a multiple of 64
+//   keys, enough pieces for about 256 workgroups; each tile of the prefix
+//   is read once per 256 rows, which pays for the extra launch when the
+//   rows are many.
+#ifndef PA_GROUP_TOKENS
+#define PA_GROUP_TOKENS 512
+#endif
+constexpr int kGroupTokens = PA_GROUP_TOKENS;
+constexpr int64_t kPassRows = 1024;
 struct PrefixPlan {
-  int pieces = 0, chunk = 0, row_tiles = 0;
+  bool pass = false;
+  int pieces = 0;
+  int tokens = 0;              // keys per piece
+  int64_t row_groups = 0;      // grouped: groups of 16 rows per kv head
+  int row_tiles = 0;           // pass: 256-row tiles per kv head
   int64_t extra_ws_bytes = 0;  // triples of the prefix pieces
 };
 
 PrefixPlan prefix_plan(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int prefix_tokens) {
   PrefixPlan pp;
   const int64_t rows = B * (Hq / Hkv);
-  const int64_t bm = pa::prefill_rows_per_workgroup();
-  pp.row_tiles = (int)((rows + bm - 1) / bm);
-  const int64_t target = std::max<int64_t>(1, 256 / std::max<int64_t>(1, Hkv * pp.row_tiles));
-  const int64_t most = std::max<int64_t>(1, (prefix_tokens + 63) / 64);
-  const int64_t want = std::min(target, most);
-  pp.chunk = (int)(((prefix_tokens + want - 1) / want + 63) / 64 * 64);
-  pp.pieces = (prefix_tokens + pp.chunk - 1) / pp.chunk;
+  pp.pass = rows >= kPassRows;
+  if (pp.pass) {
+    const int64_t bm = pa::prefill_rows_per_workgroup();
+    pp.row_tiles = (int)((rows + bm - 1) / bm);
+    const int64_t target = std::max<int64_t>(1, 256 / std::max<int64_t>(1, Hkv * pp.row_tiles));
+    const int64_t most = std::max<int64_t>(1, (prefix_tokens + 63) / 64);
+    const int64_t want = std::min(target, most);
+    pp.tokens = (int)(((prefix_tokens + want - 1) / want + 63) / 64 * 64);
+  } else {
+    pp.row_groups = (rows + 15) / 16;
+    const int want = std::max(1, (prefix_tokens + kGroupTokens - 1) / kGroupTokens);
+    pp.tokens = ((prefix_tokens + want - 1) / want + 15) / 16 * 16;
+  }
+  pp.pieces = (prefix_tokens + pp.tokens - 1) / pp.tokens;
   pp.extra_ws_bytes = B * pp.pieces * Hq * (D + 2) * (int64_t)sizeof(float);
   return pp;
 }
@@ -472,6 +501,15 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   const int64_t B = query->shape[0], Hq = query->shape[1], D = query->shape[2];
   if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads must be positive");
   const PrefixPlan pp = prefix_plan(B, Hq, num_kv_heads, D, prefix_tokens);
+  // the grouped prefix work lives in the matrix-core decode kernel, which
+  // then runs the rest of every sequence too, whatever the group size
+  if (!pp.pass) {
+    if (ln.path == PA_PATH_AUTO) ln.path = PA_PATH_MFMA;
+    if (ln.path != PA_PATH_MFMA)
+      return fail(PA_ERR_UNSUPPORTED,
+                  "with fewer than %lld (sequence, query head) rows per kv head the shared-prefix "
+                  "decode runs on the matrix-core path", (long long)kPassRows);
+  }
   pa::DecodeParams p;
   pa::DecodeVariant v;
   Plan plan;
@@ -483,7 +521,7 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   if (plan.sched != pa::kSchedBalanced)
     return fail(PA_ERR_UNSUPPORTED, "the shared-prefix decode takes batches of at most %d",
                 pa::kBalancedMaxBatch);
-  if (!pa::prefill_variant_built(v.qkind, v.kvkind, (int)D))
+  if (pp.pass && !pa::prefill_variant_built(v.qkind, v.kvkind, (int)D))
     return fail(PA_ERR_UNSUPPORTED, "no shared-prefix pass for this dtype / head_dim");
   if ((int64_t)prefix_tokens > (int64_t)p.max_blocks * p.bs)
     return fail(PA_ERR_INVALID_ARG, "prefix_tokens exceeds what the block table addresses");
@@ -497,42 +535,61 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   p.skip = prefix_tokens;
   p.prefix_pieces = pp.pieces;
   p.prefix_slot0 = (int32_t)plan.slots;
-
-  pa::PrefillParams f;
-  memset(&f, 0, sizeof f);
-  f.flags = p.flags;
-  f.q = query->data;
-  f.kc = key_cache->data;
-  f.vc = value_cache->data;
-  f.tables = static_cast<const int32_t*>(prefix_blocks->data);
-  f.tab_stride = 0;
-  f.lens = p.lens;
-  f.q_st = query->stride[0];
-  f.q_sh = query->stride[1];
-  f.B = p.B;
-  f.Hq = p.Hq;
-  f.Hkv = p.Hkv;
-  f.G = p.G;
-  f.D = p.D;
-  f.bs = p.bs;
-  f.T = p.B;
-  f.max_blocks = p.max_blocks;
-  f.num_blocks = p.num_blocks;
-  f.spb_shift = -1;
-  for (int sh = 0; sh < 24; ++sh)
-    if ((16 << sh) == p.bs) f.spb_shift = sh;
-  f.qk_scale_log2 = p.qk_scale_log2;
-  f.v_scale = p.v_scale;
-  f.ws_acc = p.ws_acc;
-  f.ws_ml = p.ws_ml;
-  f.pfx_slot0 = p.prefix_slot0;
-  f.pfx_pieces = pp.pieces;
-  f.pfx_tokens = prefix_tokens;
-  f.pfx_chunk = pp.chunk;
-  f.pfx_row_tiles = pp.row_tiles;
   hipStream_t stream = static_cast<hipStream_t>(ln.stream);
-  hipError_t e = pa::launch_prefix_pass(f, v.qkind, v.kvkind, stream);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefix pass launch failed: %s", hipGetErrorString(e));
+  hipError_t e;
+  if (pp.pass) {
+    pa::PrefillParams f;
+    memset(&f, 0, sizeof f);
+    f.flags = p.flags;
+    f.q = query->data;
+    f.kc = key_cache->data;
+    f.vc = value_cache->data;
+    f.tables = static_cast<const int32_t*>(prefix_blocks->data);
+    f.tab_stride = 0;
+    f.lens = p.lens;
+    f.q_st = query->stride[0];
+    f.q_sh = query->stride[1];
+    f.B = p.B;
+    f.Hq = p.Hq;
+    f.Hkv = p.Hkv;
+    f.G = p.G;
+    f.D = p.D;
+    f.bs = p.bs;
+    f.T = p.B;
+    f.max_blocks = p.max_blocks;
+    f.num_blocks = p.num_blocks;
+    f.spb_shift = -1;
+    for (int sh = 0; sh < 24; ++sh)
+      if ((16 << sh) == p.bs) f.spb_shift = sh;
+    f.qk_scale_log2 = p.qk_scale_log2;
+    f.v_scale = p.v_scale;
+    f.ws_acc = p.ws_acc;
+    f.ws_ml = p.ws_ml;
+    f.pfx_slot0 = p.prefix_slot0;
+    f.pfx_pieces = pp.pieces;
+    f.pfx_tokens = prefix_tokens;
+    f.pfx_chunk = pp.tokens;
+    f.pfx_row_tiles = pp.row_tiles;
+    e = pa::launch_prefix_pass(f, v.qkind, v.kvkind, stream);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "prefix pass launch failed: %s", hipGetErrorString(e));
+  } else {
+    p.prefix_blocks = static_cast<const int32_t*>(prefix_blocks->data);
+    p.grp_tokens = pp.tokens;
+    // the grouped work's rows of workgroups come out of the decode shares'
+    // budget, so that the whole grid is resident at once
+    const int64_t grp_units = (int64_t)p.Hkv * pp.row_groups;
+    const int64_t chunks = (p.units + p.waves - 1) / p.waves;
+    const int64_t grp_y = ((grp_units * pp.pieces + p.waves - 1) / p.waves + chunks - 1) / chunks;
+    int max_waves, workgroups;
+    pa::decode_launch_shape(v, &max_waves, &workgroups);
+    const int64_t per = std::max<int64_t>(1, workgroups / chunks);
+    const int64_t nwc = std::max(per - grp_y, std::max<int64_t>(per / 4, 1));
+    if (grp_units > 0x7FFFFFFF / pp.pieces || nwc + grp_y > 65535)
+      return fail(PA_ERR_UNSUPPORTED, "batch too large for the shared-prefix decode");
+    p.grp_units = (int32_t)grp_units;
+    p.grp_y = (int32_t)grp_y;
+    p.nwc = (int32_t)nwc;
+  }
   e = pa::launch_decode(p, v, stream);
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return PA_OK;

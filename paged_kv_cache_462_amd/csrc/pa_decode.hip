@@ -135,10 +135,20 @@ __device__ __forceinline__ int clamp_len(const DecodeParams& p, int b) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// One piece of work of a wave: tokens [t_lo, t_hi) of sequence b.
+// One piece of work of a wave: tokens [t_lo, t_hi) of sequence b, whose
+// block-table row is `row`.  The tiles are walked from tile `rot` on,
+// wrapping around (the grouped prefix work staggers the waves that read
+// the same tiles; 0 elsewhere).
 struct Work {
-  int b, L, t_lo, t_hi, n_tiles;
+  const int32_t* row;
+  int b, L, t_lo, t_hi, n_tiles, rot;
 };
+
+// Tile of a piece at walk position i.
+__device__ __forceinline__ int walk_tile(const Work& wk, int i) {
+  const int j = i + wk.rot;
+  return j >= wk.n_tiles ? j - wk.n_tiles : j;
+}
 
 // Owner (workgroup index within a unit chunk) of tile t when T tiles are
 // dealt to NW workgroups as [floor(w T / NW), floor((w + 1) T / NW)).
@@ -146,9 +156,37 @@ __device__ __forceinline__ int tile_owner(int t, int T, int NW) {
   return (int)(((int64_t)(t + 1) * NW - 1) / T);
 }
 
-// Balanced schedule: s_pref[b] = tiles of sequences 0..b-1 (b = 0..B), by a
+// Cost of tiles in the balanced deal.  Sequence b's tiles (counted from
+// token p.skip) are n = tiles_of(p, L); the first `low` of them start
+// below token p.cost_tokens and cost p.cost_lo each, the others p.cost_hi
+// (both 1: every tile costs the same).  Tile t starts at cost position
+// tile_pos(t); the shares are equal ranges of cost positions, and a tile
+// belongs to the share that holds its start.
+struct Costs {
+  int lo, hi;
+};
+__device__ __forceinline__ Costs costs_of(const DecodeParams& p) {
+  return Costs{max(p.cost_lo, 1), max(p.cost_hi, 1)};
+}
+__device__ __forceinline__ int tiles_of(const DecodeParams& p, int L) {
+  return (max(L - p.skip, 0) + kTile - 1) / kTile;
+}
+__device__ __forceinline__ int low_tiles(const DecodeParams& p, int n) {
+  return min(n, max(p.cost_tokens - p.skip, 0) / kTile);
+}
+__device__ __forceinline__ int seq_cost(Costs c, int low, int n) { return c.lo * low + c.hi * (n - low); }
+__device__ __forceinline__ int tile_pos(Costs c, int low, int t) {
+  return t < low ? c.lo * t : c.lo * low + c.hi * (t - low);
+}
+// first tile whose cost position is >= x
+__device__ __forceinline__ int tile_at(Costs c, int low, int x) {
+  const int xl = c.lo * low;
+  return x <= xl ? (x + c.lo - 1) / c.lo : low + (x - xl + c.hi - 1) / c.hi;
+}
+
+// Balanced schedule: s_pref[b] = cost of sequences 0..b-1 (b = 0..B), by a
 // workgroup-wide prefix sum; every thread of the workgroup must call it.
-// Returns the total tile count.
+// Returns the total cost.
 __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, int* s_wtot) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -157,7 +195,11 @@ __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, i
   int carry = 0;
   for (int base = 0; base < p.B; base += blockDim.x) {
     const int b = base + threadIdx.x;
-    int x = b < p.B ? (max(clamp_len(p, b) - p.skip, 0) + kTile - 1) / kTile : 0;
+    int x = 0;
+    if (b < p.B) {
+      const int n = tiles_of(p, clamp_len(p, b));
+      x = seq_cost(costs_of(p), low_tiles(p, n), n);
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -189,10 +231,13 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
                                                bool has_unit, F&& f) {
   if (p.sched == kSchedBalanced) {
     const int T = tile_prefix(p, s_pref, s_wtot);
-    // never more shares than tiles: then no share is empty, and the owners
-    // of one sequence's tiles are consecutive workgroups (piece k of a
-    // sequence is processed by workgroup first + k)
-    const int NW = min(p.nwc, T);
+    const Costs cs = costs_of(p);
+    const int cmax = max(cs.lo, cs.hi);
+    // shares at least cmax wide: consecutive tile starts are at most cmax
+    // apart, so no share is empty, and the owners of one sequence's tiles
+    // are consecutive workgroups (piece k of a sequence is processed by
+    // workgroup first + k)
+    const int NW = min(p.nwc, T > 0 ? max(T / cmax, 1) : 0);
     const int wi = blockIdx.y;
     if (blockIdx.x == 0 && wi == 0) {
       // the merge kernel's plan: (first slot, pieces) of every sequence,
@@ -201,8 +246,10 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
         const int sb = s_pref[b], se = s_pref[b + 1];
         int first = 0, pieces = 0;
         if (se > sb) {
+          const int n = tiles_of(p, clamp_len(p, b));
+          const int last = sb + tile_pos(cs, low_tiles(p, n), n - 1);
           first = tile_owner(sb, T, NW);
-          pieces = tile_owner(se - 1, T, NW) - first + 1;
+          pieces = tile_owner(last, T, NW) - first + 1;
         }
         p.ws_meta[2 * b] = first + b;
         p.ws_meta[2 * b + 1] = pieces;
@@ -222,13 +269,20 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
       const int sb = s_pref[b], se = s_pref[b + 1];
       if (sb >= te) break;
       if (se == sb) continue;  // empty: the merge kernel writes its zeros
+      const int L = clamp_len(p, b);
+      const int n = tiles_of(p, L);
+      const int low = low_tiles(p, n);
       const int first = tile_owner(sb, T, NW);
-      const int pieces = tile_owner(se - 1, T, NW) - first + 1;
-      const int a = max(tb, sb) - sb;
-      const int e = min(te, se) - sb;
+      const int pieces = tile_owner(sb + tile_pos(cs, low, n - 1), T, NW) - first + 1;
+      // tiles whose start lies in this share
+      const int a = tile_at(cs, low, max(tb, sb) - sb);
+      const int e = tile_at(cs, low, min(te, se) - sb);
+      if (e <= a) continue;  // the share begins inside the sequence's last tile
       Work wk;
+      wk.row = p.tables + (int64_t)b * p.tab_stride;
+      wk.rot = 0;
       wk.b = b;
-      wk.L = clamp_len(p, b);
+      wk.L = L;
       wk.t_lo = p.skip + a * kTile;
       wk.t_hi = min(p.skip + e * kTile, wk.L);
       wk.n_tiles = e - a;
@@ -240,6 +294,8 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
     if (!has_unit) return;
     Work wk;
     wk.b = blockIdx.z;
+    wk.row = p.tables + (int64_t)wk.b * p.tab_stride;
+    wk.rot = 0;
     const int part = blockIdx.y;
     wk.L = clamp_len(p, wk.b);
     wk.t_lo = part * p.part_tokens;
@@ -257,8 +313,8 @@ __device__ __forceinline__ int load_block_ids(const DecodeParams& p, const Work&
   const int i = chunk * 64 + lane;
   int id = 0;
   if (i < wk.n_tiles) {
-    const int t = wk.t_lo + kTile * i;
-    id = p.tables[(int64_t)wk.b * p.tab_stride + t / p.bs];
+    const int t = wk.t_lo + kTile * walk_tile(wk, i);
+    id = wk.row[t / p.bs];
     // an id outside the pool is a caller error; read block 0 instead of
     // faulting
     if ((unsigned)id >= (unsigned)p.num_blocks) {
@@ -274,7 +330,7 @@ __device__ __forceinline__ int load_block_ids(const DecodeParams& p, const Work&
 __device__ __forceinline__ int64_t tile_base(const DecodeParams& p, const Work& wk, int i,
                                              int ids, int64_t blk_bytes, int64_t rs) {
   const int blk = __builtin_amdgcn_readlane(ids, i & 63);
-  const int t0 = wk.t_lo + kTile * i;
+  const int t0 = wk.t_lo + kTile * walk_tile(wk, i);
   return (int64_t)blk * blk_bytes + (int64_t)(t0 % p.bs) * rs;
 }
 
@@ -395,7 +451,11 @@ __device__ __forceinline__ int64_t triple_index(const DecodeParams& p, int slot,
 // of up to 16 query heads of one kv group.
 // ============================================================================
 template <int QK, int KVK, int D>
-__global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void decode_mfma_kernel(
+// The fp8 kernel is sized for three waves per SIMD (at most 168 registers
+// a lane, matrix-core accumulators included); the hint keeps the grouped
+// copy of the loop from taking more.
+__global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves))
+__attribute__((amdgpu_waves_per_eu(KVK == K_FP8 ? 3 : 1))) void decode_mfma_kernel(
     const DecodeParams p) {
   constexpr bool kBF16 = QK == K_BF16;
   constexpr bool kFP8 = KVK == K_FP8;
@@ -438,12 +498,58 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
   const int w = threadIdx.x >> 6;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int unit = blockIdx.x * p.waves + w;
-  const bool has_unit = unit < p.units;
-  const int kvh = unit / p.head_tiles;
-  const int gh0 = (unit - kvh * p.head_tiles) * 16;
-  const int nh = min(16, p.G - gh0);
+  // Workgroups past the decode shares (blockIdx.y >= nwc) take the
+  // grouped prefix work of a shared-prefix decode: wave gw is unit
+  // gw % grp_units of piece gw / grp_units, a unit being (row group, kv
+  // head) with the kv head fastest, so the waves of a workgroup read
+  // neighbouring heads of the same tokens.
+  const bool grp = p.grp_units > 0 && (int)blockIdx.y >= p.nwc;
+  int unit, grp_piece = 0;
+  bool has_unit;
+  if (grp) {
+    const int gw = (((int)blockIdx.y - p.nwc) * (int)gridDim.x + (int)blockIdx.x) * p.waves + w;
+    grp_piece = gw / p.grp_units;
+    unit = gw - grp_piece * p.grp_units;
+    has_unit = grp_piece < p.prefix_pieces;
+  } else {
+    unit = blockIdx.x * p.waves + w;
+    has_unit = unit < p.units;
+  }
+  const int kvh = grp ? unit % p.Hkv : unit / p.head_tiles;
+  const int gh0 = grp ? 0 : (unit - kvh * p.head_tiles) * 16;
+  const int nh = grp ? 16 : min(16, p.G - gh0);
   const int head0 = kvh * p.G + gh0;
+  // grouped work: this lane's column n is row r of the kv head's
+  // (sequence, query head) rows, sequence-major: sequence gb, query head
+  // gh, keys [0, glim) of the prefix; the wave's smallest and largest
+  // limits decide which tiles need the per-column mask and where its work
+  // ends
+  // (gb and gh are found again where they are used, which keeps them out
+  // of the registers the tile loop holds)
+  auto grp_row = [&](int& gb, int& gh) {
+    const int r = (unit / p.Hkv) * 16 + n;
+    gb = r / p.G;
+    gh = kvh * p.G + (r - gb * p.G);
+  };
+  bool gvalid = false;
+  int glim = 0, glmin = 0, glmax = 0;
+  if (grp) {
+    gvalid = has_unit && (unit / p.Hkv) * 16 + n < p.B * p.G;
+    if (gvalid) {
+      int gb, gh;
+      grp_row(gb, gh);
+      glim = min(clamp_len(p, gb), p.skip);
+    }
+    glmin = gvalid ? glim : 0x7FFFFFFF;
+    glmax = gvalid ? glim : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      glmin = min(glmin, __shfl_xor(glmin, off));
+      glmax = max(glmax, __shfl_xor(glmax, off));
+    }
+    glmin = __builtin_amdgcn_readfirstlane(glmin);
+    glmax = __builtin_amdgcn_readfirstlane(glmax);
+  }
 
   const int64_t rs = (int64_t)p.Hkv * RB;  // bytes between tokens
   const int64_t blk_bytes = rs * p.bs;
@@ -481,19 +587,28 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
     Bytes<VBYTES> v[4];
   };
 
-  for_each_piece(p, s_pref, s_wtot, has_unit, [&](const Work& wk, int slot) {
+  // kG: the grouped prefix work's copy of the loop (a compile-time flag, so
+  // the decode's copy keeps no register for it)
+  auto piece = [&](const Work& wk, int slot, auto grp_tag) {
+    constexpr bool kG = decltype(grp_tag)::value;
     // Query group as the B operand of the score MFMAs: lane (n, g) holds
-    // head n, 8 dims per MFMA: those of 16-byte K chunk 4r + g (16-bit K:
-    // MFMA r; fp8 K: the low / high half of that chunk for MFMAs 2r, 2r + 1).
+    // column n (head n, or row n of the grouped work), 8 dims per MFMA:
+    // those of 16-byte K chunk 4r + g (16-bit K: MFMA r; fp8 K: the low /
+    // high half of that chunk for MFMAs 2r, 2r + 1).
     i32x4 qop[NJQ];
     {
-      const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + (int64_t)wk.b * p.q_sb +
-                             (int64_t)(head0 + min(n, nh - 1)) * p.q_sh;
+      int gb = 0, gh = 0;
+      if constexpr (kG) grp_row(gb, gh);
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) +
+          (kG ? (int64_t)gb * p.q_sb + (int64_t)gh * p.q_sh
+              : (int64_t)wk.b * p.q_sb + (int64_t)(head0 + min(n, nh - 1)) * p.q_sh);
+      const bool live = kG ? gvalid : n < nh;
 #pragma unroll
       for (int j = 0; j < NJQ; ++j) {
         const int d0 = kFP8 ? ((j >> 1) * 64 + g * 16 + (j & 1) * 8) : (j * 32 + g * 8);
         const i32x4 v = *reinterpret_cast<const i32x4*>(qrow + d0);
-        qop[j] = n < nh ? v : i32x4{0, 0, 0, 0};
+        qop[j] = live ? v : i32x4{0, 0, 0, 0};
       }
     }
 
@@ -533,7 +648,7 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
     };
 
     auto compute_tile = [&](int i, Regs& r) {
-      const int t0 = wk.t_lo + kTile * i;
+      const int t0 = wk.t_lo + kTile * walk_tile(wk, i);
       // only a piece's last tile can reach past its end (wave-uniform)
       const bool partial = t0 + kTile > wk.t_hi;
       // scores: D[token 4g+q][head n]
@@ -559,6 +674,13 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (t0 + 4 * g + q >= wk.t_hi) sv[q] = -INFINITY;
+      }
+      // grouped work: each column's own length (wave-uniform test: only
+      // the tiles that reach past the shortest row of the wave)
+      if (kG && t0 + kTile > glmin) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (t0 + 4 * g + q >= glim) sv[q] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -667,8 +789,15 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
     // lane groups hold partial sums over different tokens
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (n >= nh) return;
-    const int h = head0 + n;
+    int gb = 0, gh = 0;
+    if constexpr (kG) {
+      if (!gvalid) return;
+      grp_row(gb, gh);
+      slot = p.prefix_slot0 + gb * p.prefix_pieces + grp_piece;
+    } else {
+      if (n >= nh) return;
+    }
+    const int h = kG ? gh : head0 + n;
     // lane (n, g) holds out[h][(4g+i)*NJV + j] in acc[j][i]
     if (slot >= 0) {
       const int64_t ti = triple_index(p, slot, h);
@@ -694,7 +823,27 @@ __global__ __launch_bounds__(64 * (KVK == K_FP8 ? kFp8Waves : kMaxWaves)) void d
         store_out_vec<QK, NJV>(p.out, ob + (4 * g + i) * NJV, x);
       }
     }
-  });
+  };
+  if (grp) {
+    // piece grp_piece of grp_tokens tokens of the prefix (its blocks are
+    // the one table row), up to the longest row of the wave
+    if (!has_unit) return;
+    Work wk;
+    wk.row = p.prefix_blocks;
+    wk.b = 0;
+    wk.L = p.skip;
+    wk.t_lo = grp_piece * p.grp_tokens;
+    const int hi = min(min(p.skip, wk.t_lo + p.grp_tokens), glmax);
+    wk.n_tiles = hi > wk.t_lo ? (hi - wk.t_lo + kTile - 1) / kTile : 0;
+    wk.t_hi = wk.t_lo + wk.n_tiles * kTile;  // whole tiles: no token mask
+    // the row groups of one kv head read the same tiles: each starts at
+    // its own tile (the result does not depend on the order)
+    wk.rot = wk.n_tiles > 0 ? (unit / p.Hkv) % wk.n_tiles : 0;
+    piece(wk, 0, std::true_type{});
+  } else {
+    for_each_piece(p, s_pref, s_wtot, has_unit,
+                   [&](const Work& wk, int slot) { piece(wk, slot, std::false_type{}); });
+  }
 }
 
 // ============================================================================
@@ -1107,8 +1256,19 @@ hipError_t launch_all(const DecodeParams& p, const DecodeVariant& v, hipStream_t
   if (p.waves < 1 || p.waves > max_waves) return hipErrorInvalidValue;
   if (p.sched == kSchedBalanced && (p.B > kBalancedMaxBatch || p.nwc < 1 || p.nwc > kBalancedSlots))
     return hipErrorInvalidValue;
+  if (p.grp_units > 0) {
+    // grouped prefix work: matrix-core kernel, balanced schedule, and
+    // enough workgroups for every (unit, piece)
+    const int64_t grp_waves = (int64_t)p.grp_units * p.prefix_pieces;
+    const int64_t chunks = (p.units + p.waves - 1) / p.waves;
+    if (v.path != 2 || p.sched != kSchedBalanced || !p.prefix_blocks || p.grp_tokens < 16 ||
+        p.grp_tokens % 16 || p.prefix_pieces < 1 || p.grp_y < 1 ||
+        (int64_t)p.grp_y * chunks * p.waves < grp_waves || p.nwc + p.grp_y > 65535)
+      return hipErrorInvalidValue;
+  }
   const int chunks = (p.units + p.waves - 1) / p.waves;
-  const dim3 grid = p.sched == kSchedBalanced ? dim3(chunks, p.nwc, 1) : dim3(chunks, p.num_parts, p.B);
+  const dim3 grid = p.sched == kSchedBalanced ? dim3(chunks, p.nwc + p.grp_y, 1)
+                                              : dim3(chunks, p.num_parts, p.B);
   const dim3 block(p.waves * 64);
   hipError_t e;
   if (v.path == 2) {

@@ -2,8 +2,11 @@
 ABI) against the fp64 decode oracle: the result must be plain decode's, for
 sequences shorter than, equal to and longer than the shared prefix, empty
 ones included, across the dtype / group / block-size / head_dim variants,
-and every element at the full workload sizes, whose batches are built
-through the host allocator, block manager and prefix cache."""
+both ways of taking the prefix part (grouped work inside the decode launch
+below 1024 (sequence, query head) rows per kv head, the prefix pass from
+there on), and every element at the full workload sizes (c5 grouped, c6 the
+pass), whose batches are built through the host allocator, block manager
+and prefix cache."""
 
 import numpy as np
 import pytest
@@ -23,10 +26,16 @@ CASES = {
     "f16_mha_valu": (shrink(get_config("c2"), num_q_heads=8, num_kv_heads=8), 256,
                      [300, 256, 100, 1200, 17]),
     "bf16_g8_d64": (shrink(get_config("c3"), head_dim=64), 384, [800, 5, 384, 1000]),
-    # 40 sequences x 8 heads = 320 rows per kv head: two row tiles of the
-    # prefix pass
-    "bf16_g8_two_row_tiles": (get_config("c3"), 256,
-                              [int(x) for x in np.random.default_rng(3).integers(0, 700, 40)]),
+    # 40 sequences x 8 heads = 320 rows per kv head: 20 row groups of the
+    # grouped prefix work
+    "bf16_g8_320_rows": (get_config("c3"), 256,
+                         [int(x) for x in np.random.default_rng(3).integers(0, 700, 40)]),
+    # 1024 rows per kv head or more: the prefix pass, in 256-row tiles (5
+    # and 5, the last one partly filled)
+    "bf16_g8_pass_1040_rows": (get_config("c3"), 256,
+                               [int(x) for x in np.random.default_rng(4).integers(0, 700, 130)]),
+    "fp8_g4_pass_1040_rows": (get_config("c5"), 512,
+                              [int(x) for x in np.random.default_rng(5).integers(0, 1500, 260)]),
     "fp8_f16q_g4": (shrink(get_config("c5"), q_dtype="f16", block_size=16, shared_prefix_tokens=0),
                     160, [161, 159, 640, 1]),
 }

@@ -301,20 +301,35 @@ def test_shared_prefix_rejects():
     # batches beyond the balanced schedule
     assert _lib.load().pa_decode_shared_prefix_workspace_bytes(4096, 8, 8, 128, 16, 8, 32) == \
         _lib.PA_ERR_UNSUPPORTED
+    # below 1024 rows per kv head the grouped prefix work runs in the
+    # matrix-core kernel: asking for the VALU path is refused
+    _expect(_call_shared(a, pb, 32, launch=PaLaunch(None, FAKE, 1 << 40, 0, 1)), _lib.PA_ERR_UNSUPPORTED)
+    assert "matrix-core" in _lib.last_error()
 
 
 def test_shared_prefix_workspace_formula():
     lib = _lib.load()
-    # batch 128, 32 q / 8 kv heads, d 128, prefix 1024: 2 row tiles of 256
-    # rows per kv head, 8 * 2 = 16 workgroups per key piece, so 16 pieces of
-    # 64 keys
+    # fewer than 1024 (sequence, query head) rows per kv head: the grouped
+    # prefix work, keys in pieces of about 512 (a multiple of 16), one
+    # triple per (sequence, query head, piece) after the decode's own.
+    # 128 x 4 rows, prefix 1024 -> 2 pieces of 512
     base = lib.pa_decode_workspace_bytes(128, 32, 8, 128, 32, 512, 0)
     got = lib.pa_decode_shared_prefix_workspace_bytes(128, 32, 8, 128, 32, 512, 1024)
-    assert got == base + 128 * 16 * 32 * 130 * 4
-    # batch 200, 64 q / 8 kv heads, prefix 512: 7 row tiles, 4 pieces of 128
+    assert got == base + 128 * 2 * 32 * 130 * 4
+    # prefix 96 -> one piece; prefix 1200 -> 3 pieces of 400
+    base = lib.pa_decode_workspace_bytes(3, 4, 2, 64, 16, 80, 0)
+    assert lib.pa_decode_shared_prefix_workspace_bytes(3, 4, 2, 64, 16, 80, 96) == base + 3 * 1 * 4 * 66 * 4
+    assert lib.pa_decode_shared_prefix_workspace_bytes(3, 4, 2, 64, 16, 80, 1200) == base + 3 * 3 * 4 * 66 * 4
+    # 1024 rows or more: the prefix pass, 256-row tiles and enough pieces of
+    # a multiple of 64 keys for about 256 workgroups.  200 x 8 rows: 7 row
+    # tiles x 8 kv heads = 56 workgroups a piece -> 4 pieces of 128
     base = lib.pa_decode_workspace_bytes(200, 64, 8, 128, 16, 48, 0)
     got = lib.pa_decode_shared_prefix_workspace_bytes(200, 64, 8, 128, 16, 48, 512)
     assert got == base + 200 * 4 * 64 * 130 * 4
+    # 256 x 4 rows = 1024: 4 row tiles x 8 = 32 a piece -> 8 pieces of 128
+    base = lib.pa_decode_workspace_bytes(256, 32, 8, 128, 32, 512, 0)
+    got = lib.pa_decode_shared_prefix_workspace_bytes(256, 32, 8, 128, 32, 512, 1024)
+    assert got == base + 256 * 8 * 32 * 130 * 4
 
 
 # --- allocator and block manager against the oracle's model ------------------
