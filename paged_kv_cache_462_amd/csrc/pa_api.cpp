@@ -299,11 +299,6 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
-#ifdef PA_EXP_COST_TOKENS
-  p.cost_tokens = PA_EXP_COST_TOKENS;
-  p.cost_lo = PA_EXP_COST_LO;
-  p.cost_hi = PA_EXP_COST_HI;
-#endif
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;

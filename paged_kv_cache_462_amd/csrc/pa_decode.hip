@@ -156,37 +156,14 @@ __device__ __forceinline__ int tile_owner(int t, int T, int NW) {
   return (int)(((int64_t)(t + 1) * NW - 1) / T);
 }
 
-// Cost of tiles in the balanced deal.  Sequence b's tiles (counted from
-// token p.skip) are n = tiles_of(p, L); the first `low` of them start
-// below token p.cost_tokens and cost p.cost_lo each, the others p.cost_hi
-// (both 1: every tile costs the same).  Tile t starts at cost position
-// tile_pos(t); the shares are equal ranges of cost positions, and a tile
-// belongs to the share that holds its start.
-struct Costs {
-  int lo, hi;
-};
-__device__ __forceinline__ Costs costs_of(const DecodeParams& p) {
-  return Costs{max(p.cost_lo, 1), max(p.cost_hi, 1)};
-}
+// Tiles of sequence b (tokens from p.skip on) when its length is L.
 __device__ __forceinline__ int tiles_of(const DecodeParams& p, int L) {
   return (max(L - p.skip, 0) + kTile - 1) / kTile;
 }
-__device__ __forceinline__ int low_tiles(const DecodeParams& p, int n) {
-  return min(n, max(p.cost_tokens - p.skip, 0) / kTile);
-}
-__device__ __forceinline__ int seq_cost(Costs c, int low, int n) { return c.lo * low + c.hi * (n - low); }
-__device__ __forceinline__ int tile_pos(Costs c, int low, int t) {
-  return t < low ? c.lo * t : c.lo * low + c.hi * (t - low);
-}
-// first tile whose cost position is >= x
-__device__ __forceinline__ int tile_at(Costs c, int low, int x) {
-  const int xl = c.lo * low;
-  return x <= xl ? (x + c.lo - 1) / c.lo : low + (x - xl + c.hi - 1) / c.hi;
-}
 
-// Balanced schedule: s_pref[b] = cost of sequences 0..b-1 (b = 0..B), by a
+// Balanced schedule: s_pref[b] = tiles of sequences 0..b-1 (b = 0..B), by a
 // workgroup-wide prefix sum; every thread of the workgroup must call it.
-// Returns the total cost.
+// Returns the total tile count.
 __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, int* s_wtot) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -195,11 +172,7 @@ __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, i
   int carry = 0;
   for (int base = 0; base < p.B; base += blockDim.x) {
     const int b = base + threadIdx.x;
-    int x = 0;
-    if (b < p.B) {
-      const int n = tiles_of(p, clamp_len(p, b));
-      x = seq_cost(costs_of(p), low_tiles(p, n), n);
-    }
+    int x = b < p.B ? tiles_of(p, clamp_len(p, b)) : 0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -231,13 +204,10 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
                                                bool has_unit, F&& f) {
   if (p.sched == kSchedBalanced) {
     const int T = tile_prefix(p, s_pref, s_wtot);
-    const Costs cs = costs_of(p);
-    const int cmax = max(cs.lo, cs.hi);
-    // shares at least cmax wide: consecutive tile starts are at most cmax
-    // apart, so no share is empty, and the owners of one sequence's tiles
-    // are consecutive workgroups (piece k of a sequence is processed by
-    // workgroup first + k)
-    const int NW = min(p.nwc, T > 0 ? max(T / cmax, 1) : 0);
+    // never more shares than tiles: then no share is empty, and the owners
+    // of one sequence's tiles are consecutive workgroups (piece k of a
+    // sequence is processed by workgroup first + k)
+    const int NW = min(p.nwc, T);
     const int wi = blockIdx.y;
     if (blockIdx.x == 0 && wi == 0) {
       // the merge kernel's plan: (first slot, pieces) of every sequence,
@@ -246,10 +216,8 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
         const int sb = s_pref[b], se = s_pref[b + 1];
         int first = 0, pieces = 0;
         if (se > sb) {
-          const int n = tiles_of(p, clamp_len(p, b));
-          const int last = sb + tile_pos(cs, low_tiles(p, n), n - 1);
           first = tile_owner(sb, T, NW);
-          pieces = tile_owner(last, T, NW) - first + 1;
+          pieces = tile_owner(se - 1, T, NW) - first + 1;
         }
         p.ws_meta[2 * b] = first + b;
         p.ws_meta[2 * b + 1] = pieces;
@@ -269,20 +237,15 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
       const int sb = s_pref[b], se = s_pref[b + 1];
       if (sb >= te) break;
       if (se == sb) continue;  // empty: the merge kernel writes its zeros
-      const int L = clamp_len(p, b);
-      const int n = tiles_of(p, L);
-      const int low = low_tiles(p, n);
       const int first = tile_owner(sb, T, NW);
-      const int pieces = tile_owner(sb + tile_pos(cs, low, n - 1), T, NW) - first + 1;
-      // tiles whose start lies in this share
-      const int a = tile_at(cs, low, max(tb, sb) - sb);
-      const int e = tile_at(cs, low, min(te, se) - sb);
-      if (e <= a) continue;  // the share begins inside the sequence's last tile
+      const int pieces = tile_owner(se - 1, T, NW) - first + 1;
+      const int a = max(tb, sb) - sb;
+      const int e = min(te, se) - sb;
       Work wk;
       wk.row = p.tables + (int64_t)b * p.tab_stride;
       wk.rot = 0;
       wk.b = b;
-      wk.L = L;
+      wk.L = clamp_len(p, b);
       wk.t_lo = p.skip + a * kTile;
       wk.t_hi = min(p.skip + e * kTile, wk.L);
       wk.n_tiles = e - a;

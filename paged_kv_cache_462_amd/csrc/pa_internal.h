@@ -69,12 +69,6 @@ struct DecodeParams {
   int32_t prefix_pieces;
   int32_t prefix_slot0;
   int32_t* flags;         // caller's error flags [kNumFlags], or null
-  // Cost of the balanced deal: a tile that starts below token cost_tokens
-  // costs cost_lo, any other tile cost_hi (both >= 1; 0 reads as 1).  The
-  // shares are equal ranges of cost.
-  int32_t cost_tokens;
-  int32_t cost_lo;
-  int32_t cost_hi;
   // Grouped prefix work of a shared-prefix decode (matrix-core kernel,
   // balanced schedule): grp_y more rows of workgroups after the nwc decode
   // shares.  A unit is (row group, kv head): the kv head's (sequence, query

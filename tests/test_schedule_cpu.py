@@ -100,3 +100,87 @@ def test_balanced_schedule_edges():
     _check([16 * 256 + 1])
     _check([32768] * 4)
     _check([4096] * 64)         # every sequence in four pieces
+
+
+# --- shared-prefix decode: the grouped prefix work ---------------------------
+#
+# Below 1024 (sequence, query head) rows per kv head, pa_decode_shared_prefix
+# adds grp_y rows of workgroups after the nwc decode shares of each unit
+# chunk.  Wave gw of that part (workgroups in grid order, waves in
+# workgroup order) takes piece gw // U of unit gw % U, U = Hkv * row_groups;
+# a unit is (row group, kv head) with the kv head fastest, and column n of
+# row group rg is row rg * 16 + n of the kv head's rows, sequence-major.  The
+# prefix is cut into pieces of a multiple of 16 tokens, about 512 each.
+# The decode shares give up the grouped rows of workgroups, so the grid is
+# resident at once (at least a quarter of the shares stay).
+
+GROUP_TOKENS = 512
+
+
+def grouped_plan(B, Hq, Hkv, P, waves, chunks, workgroups):
+    G = Hq // Hkv
+    row_groups = (B * G + 15) // 16
+    want = max(1, (P + GROUP_TOKENS - 1) // GROUP_TOKENS)
+    tokens = ((P + want - 1) // want + 15) // 16 * 16
+    pieces = (P + tokens - 1) // tokens
+    units = Hkv * row_groups
+    grp_y = ((units * pieces + waves - 1) // waves + chunks - 1) // chunks
+    per = max(1, workgroups // chunks)
+    nwc = max(per - grp_y, max(per // 4, 1))
+    return dict(G=G, row_groups=row_groups, tokens=tokens, pieces=pieces, units=units,
+                grp_y=grp_y, nwc=nwc)
+
+
+def grouped_waves(B, Hq, Hkv, P, waves, chunks, workgroups):
+    """(b, h, piece, token range, slot offset) for every live column of
+    every grouped wave, as the kernel derives them."""
+    pl = grouped_plan(B, Hq, Hkv, P, waves, chunks, workgroups)
+    G, U = pl["G"], pl["units"]
+    out = []
+    for y in range(pl["nwc"], pl["nwc"] + pl["grp_y"]):
+        for x in range(chunks):
+            for w in range(waves):
+                gw = ((y - pl["nwc"]) * chunks + x) * waves + w
+                piece, unit = divmod(gw, U)
+                if piece >= pl["pieces"]:
+                    continue  # no unit: the wave exits
+                kvh, rg = unit % Hkv, unit // Hkv
+                lo = piece * pl["tokens"]
+                hi = min(P, lo + pl["tokens"])
+                for n in range(16):
+                    r = rg * 16 + n
+                    if r >= B * G:
+                        continue
+                    b, j = divmod(r, G)
+                    out.append((b, kvh * G + j, piece, lo, hi, b * pl["pieces"] + piece))
+    return out, pl
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,P,waves,chunks,workgroups", [
+    (128, 32, 8, 1024, 4, 2, 768),   # the 1024-token fp8 prompt batch
+    (40, 64, 8, 256, 8, 1, 256),     # bf16, group 8
+    (5, 8, 8, 256, 8, 1, 256),       # MHA on the matrix-core path
+    (4, 32, 8, 1200, 8, 1, 256),     # prefix not a multiple of 512
+    (255, 16, 4, 96, 4, 1, 768),     # 1020 rows, one piece of 96
+    (7, 96, 96, 2048, 8, 12, 256),   # many kv heads: a quarter of the shares stay
+])
+def test_grouped_prefix_work_covers_every_row_once(B, Hq, Hkv, P, waves, chunks, workgroups):
+    cols, pl = grouped_waves(B, Hq, Hkv, P, waves, chunks, workgroups)
+    assert B * (Hq // Hkv) < 1024
+    seen = {}
+    for b, h, piece, lo, hi, slot in cols:
+        assert 0 <= b < B and 0 <= h < Hq and lo < hi <= P and lo % 16 == 0
+        assert (b, h, piece) not in seen
+        seen[(b, h, piece)] = (lo, hi)
+        assert 0 <= slot < B * pl["pieces"]  # prefix slots follow the decode's
+    assert len(seen) == B * Hq * pl["pieces"]
+    for b in range(B):
+        for h in range(Hq):
+            ranges = sorted(seen[(b, h, k)] for k in range(pl["pieces"]))
+            assert ranges[0][0] == 0 and ranges[-1][1] == P
+            assert all(ranges[i][1] == ranges[i + 1][0] for i in range(len(ranges) - 1))
+    # the decode shares and the grouped rows fit the grid and the workspace
+    assert pl["nwc"] >= 1 and pl["nwc"] <= SLOTS and pl["nwc"] + pl["grp_y"] <= 65535
+    assert pl["grp_y"] * chunks * waves >= pl["units"] * pl["pieces"]
+    if pl["nwc"] > max(workgroups // chunks // 4, 1):
+        assert (pl["nwc"] + pl["grp_y"]) * chunks <= workgroups  # one round
