@@ -132,6 +132,9 @@ constexpr int kSinglePassMaxTokens = 256;
 
 // balanced_only: the automatic plan is always the balanced schedule (the
 // shared-prefix decode needs it), whatever the context length.
+// Tiles' worth of time charged for each sequence a balanced share starts.
+constexpr int kPieceCost = 3;
+
 int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out,
               bool balanced_only = false) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0)
@@ -299,6 +302,11 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
+  // a piece's start costs a wave about three tiles' time (measured on the
+  // shared-prompt and lognormal-length batches: 3 to 4 us a piece against
+  // 0.8 to 1.2 us a tile); charging it in the deal shortens the shares
+  // that start several sequences
+  p.piece_cost = plan.sched == pa::kSchedBalanced ? kPieceCost : 0;
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
@@ -329,18 +337,15 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
 // prefix keys serve rows = B * G (sequence, query head) rows.
 // - Grouped (rows < kPassRows): inside the matrix-core decode launch, the
 //   rows in groups of 16 (one wave each, the kernel's query columns) over
-//   pieces of about kGroupTokens keys, so a wave's piece is about as many
-//   tiles as a decode share; every group reads the prefix tiles it needs
-//   again (from the caches).
+//   pieces of about kGroupTokens keys (24 tiles), about what a decode
+//   share holds, so that neither kind of wave is left to finish alone;
+//   every group reads the prefix tiles it needs again (from the caches).
 // - Pass (rows >= kPassRows): a launch of the prefill kernel before the
 //   decode, 256-row tiles of the rows against pieces of a multiple of 64
 //   keys, enough pieces for about 256 workgroups; each tile of the prefix
 //   is read once per 256 rows, which pays for the extra launch when the
 //   rows are many.
-#ifndef PA_GROUP_TOKENS
-#define PA_GROUP_TOKENS 512
-#endif
-constexpr int kGroupTokens = PA_GROUP_TOKENS;
+constexpr int kGroupTokens = 384;
 constexpr int64_t kPassRows = 1024;
 struct PrefixPlan {
   bool pass = false;

@@ -161,9 +161,12 @@ __device__ __forceinline__ int tiles_of(const DecodeParams& p, int L) {
   return (max(L - p.skip, 0) + kTile - 1) / kTile;
 }
 
-// Balanced schedule: s_pref[b] = tiles of sequences 0..b-1 (b = 0..B), by a
+// Balanced schedule: s_pref[b] = cost of sequences 0..b-1 (b = 0..B), by a
 // workgroup-wide prefix sum; every thread of the workgroup must call it.
-// Returns the total tile count.
+// A non-empty sequence costs its tiles plus p.piece_cost: the start of a
+// piece (its query and block ids, then its first tile, with nothing in
+// flight) takes about as long as that many tiles, so a share that starts
+// several sequences gets fewer tiles.  Returns the total cost.
 __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, int* s_wtot) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -173,6 +176,7 @@ __device__ __forceinline__ int tile_prefix(const DecodeParams& p, int* s_pref, i
   for (int base = 0; base < p.B; base += blockDim.x) {
     const int b = base + threadIdx.x;
     int x = b < p.B ? tiles_of(p, clamp_len(p, b)) : 0;
+    if (x > 0) x += p.piece_cost;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int y = __shfl_up(x, off);
@@ -204,10 +208,13 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
                                                bool has_unit, F&& f) {
   if (p.sched == kSchedBalanced) {
     const int T = tile_prefix(p, s_pref, s_wtot);
-    // never more shares than tiles: then no share is empty, and the owners
-    // of one sequence's tiles are consecutive workgroups (piece k of a
-    // sequence is processed by workgroup first + k)
-    const int NW = min(p.nwc, T);
+    // Cost positions: sequence b's first piece_cost positions from s_pref[b]
+    // are its start, its tiles follow.  Shares at least piece_cost + 1
+    // wide: every one then holds a tile, and the owners of one sequence's
+    // tiles are consecutive workgroups (piece k of a sequence is processed
+    // by workgroup first + k).
+    const int K = p.piece_cost;
+    const int NW = min(p.nwc, T > 0 ? max(T / (K + 1), 1) : 0);
     const int wi = blockIdx.y;
     if (blockIdx.x == 0 && wi == 0) {
       // the merge kernel's plan: (first slot, pieces) of every sequence,
@@ -216,7 +223,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
         const int sb = s_pref[b], se = s_pref[b + 1];
         int first = 0, pieces = 0;
         if (se > sb) {
-          first = tile_owner(sb, T, NW);
+          first = tile_owner(sb + K, T, NW);
           pieces = tile_owner(se - 1, T, NW) - first + 1;
         }
         p.ws_meta[2 * b] = first + b;
@@ -237,10 +244,12 @@ __device__ __forceinline__ void for_each_piece(const DecodeParams& p, int* s_pre
       const int sb = s_pref[b], se = s_pref[b + 1];
       if (sb >= te) break;
       if (se == sb) continue;  // empty: the merge kernel writes its zeros
-      const int first = tile_owner(sb, T, NW);
+      const int r0 = sb + K;  // position of the sequence's first tile
+      const int a = max(tb, r0) - r0;
+      const int e = min(te, se) - r0;
+      if (e <= a) continue;  // the share ends inside the sequence's start
+      const int first = tile_owner(r0, T, NW);
       const int pieces = tile_owner(se - 1, T, NW) - first + 1;
-      const int a = max(tb, sb) - sb;
-      const int e = min(te, se) - sb;
       Work wk;
       wk.row = p.tables + (int64_t)b * p.tab_stride;
       wk.rot = 0;

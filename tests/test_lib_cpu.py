@@ -310,16 +310,16 @@ def test_shared_prefix_rejects():
 def test_shared_prefix_workspace_formula():
     lib = _lib.load()
     # fewer than 1024 (sequence, query head) rows per kv head: the grouped
-    # prefix work, keys in pieces of about 512 (a multiple of 16), one
+    # prefix work, keys in pieces of about 384 (a multiple of 16), one
     # triple per (sequence, query head, piece) after the decode's own.
-    # 128 x 4 rows, prefix 1024 -> 2 pieces of 512
+    # 128 x 4 rows, prefix 1024 -> 3 pieces of 352
     base = lib.pa_decode_workspace_bytes(128, 32, 8, 128, 32, 512, 0)
     got = lib.pa_decode_shared_prefix_workspace_bytes(128, 32, 8, 128, 32, 512, 1024)
-    assert got == base + 128 * 2 * 32 * 130 * 4
-    # prefix 96 -> one piece; prefix 1200 -> 3 pieces of 400
+    assert got == base + 128 * 3 * 32 * 130 * 4
+    # prefix 96 -> one piece; prefix 1200 -> 4 pieces of 304 (the last 288)
     base = lib.pa_decode_workspace_bytes(3, 4, 2, 64, 16, 80, 0)
     assert lib.pa_decode_shared_prefix_workspace_bytes(3, 4, 2, 64, 16, 80, 96) == base + 3 * 1 * 4 * 66 * 4
-    assert lib.pa_decode_shared_prefix_workspace_bytes(3, 4, 2, 64, 16, 80, 1200) == base + 3 * 3 * 4 * 66 * 4
+    assert lib.pa_decode_shared_prefix_workspace_bytes(3, 4, 2, 64, 16, 80, 1200) == base + 3 * 4 * 4 * 66 * 4
     # 1024 rows or more: the prefix pass, 256-row tiles and enough pieces of
     # a multiple of 64 keys for about 256 workgroups.  200 x 8 rows: 7 row
     # tiles x 8 kv heads = 56 workgroups a piece -> 4 pieces of 128

@@ -1,13 +1,17 @@
 """The balanced decode schedule's arithmetic, restated on the CPU.
 
 The kernel deals the batch's 16-token tiles (sequences back to back) to NW
-workgroups as [floor(w T / NW), floor((w + 1) T / NW)) with NW = min(nwc, T)
-(nwc: 256 / unit chunks for 8-wave workgroups, 768 / unit chunks for the fp8
-kernel's 4-wave ones), and gives piece k of sequence b the triple slot
-owner(S_b) + b + k.  These checks hold that arithmetic to its invariants on
-many length mixes and both grid sizes: every tile is covered once, the pieces
-of a sequence go to consecutive workgroups with non-empty shares, and slots
-are unique and below 768 + B (the workspace size pa_decode_plan reports)."""
+workgroups in equal ranges of cost, [floor(w T / NW), floor((w + 1) T / NW)).
+A non-empty sequence costs its tiles plus K (the start of a piece, charged
+as K tiles: positions S_b .. S_b + K - 1 are its start, its tiles follow),
+and NW = min(nwc, T / (K + 1)) (nwc: 256 / unit chunks for 8-wave
+workgroups, 768 / unit chunks for the fp8 kernel's 4-wave ones).  A tile
+belongs to the share that holds its position, and piece k of sequence b gets
+the triple slot owner(S_b + K) + b + k.  These checks hold that arithmetic to
+its invariants on many length mixes, grid sizes and K (3 is the library's):
+every tile is covered once, the pieces of a sequence go to consecutive
+workgroups, every share holds a tile, and slots are unique and below
+768 + B (the workspace size pa_decode_plan reports)."""
 
 import numpy as np
 import pytest
@@ -15,16 +19,18 @@ import pytest
 TILE = 16
 NWC = 256
 SLOTS = 768   # shares per unit chunk the workspace holds slots for
+K_LIB = 3     # the library's charge for a sequence start
 
 
-def schedule(lengths, nwc=NWC):
+def schedule(lengths, nwc=NWC, K=K_LIB):
     tiles = [(int(L) + TILE - 1) // TILE for L in lengths]
-    S = np.concatenate([[0], np.cumsum(tiles)]).astype(np.int64)
+    cost = [t + K if t else 0 for t in tiles]
+    S = np.concatenate([[0], np.cumsum(cost)]).astype(np.int64)
     T = int(S[-1])
     out = []  # (workgroup, b, first tile in b, end tile in b, slot or -1)
     if T == 0:
         return out, T, 0
-    NW = min(nwc, T)
+    NW = min(nwc, max(T // (K + 1), 1))
 
     def owner(t):
         return ((t + 1) * NW - 1) // T
@@ -32,20 +38,25 @@ def schedule(lengths, nwc=NWC):
     for wi in range(NW):
         tb, te = wi * T // NW, (wi + 1) * T // NW
         assert te > tb
+        held = 0
         b = int(np.searchsorted(S[1:], tb, side="right"))
         while b < len(lengths) and S[b] < te:
             sb, se = int(S[b]), int(S[b + 1])
-            if se > sb:
-                first = owner(sb)
+            r0 = sb + K
+            a, e = max(tb, r0) - r0, min(te, se) - r0
+            if se > sb and e > a:
+                first = owner(r0)
                 pieces = owner(se - 1) - first + 1
                 slot = first + b + (wi - first) if pieces > 1 else -1
-                out.append((wi, b, max(tb, sb) - sb, min(te, se) - sb, slot))
+                out.append((wi, b, a, e, slot))
+                held += e - a
             b += 1
+        assert held > 0  # every share holds a tile
     return out, T, NW
 
 
-def _check(lengths, nwc=NWC):
-    pieces, T, NW = schedule(lengths, nwc)
+def _check(lengths, nwc=NWC, K=K_LIB):
+    pieces, T, NW = schedule(lengths, nwc, K)
     B = len(lengths)
     covered = {}
     slots = set()
@@ -72,12 +83,13 @@ def _check(lengths, nwc=NWC):
             assert ps[0][1] == 0 and ps[-1][2] == nt
         elif len(ps) == 1:
             assert ps[0][3] == -1 and ps[0][1] == 0 and ps[0][2] == nt
-    assert len(covered) == T
+    assert len(covered) == sum((int(L) + TILE - 1) // TILE for L in lengths)
 
 
+@pytest.mark.parametrize("K", [0, K_LIB, 7])
 @pytest.mark.parametrize("nwc", [256, 64, 768, 384])
 @pytest.mark.parametrize("seed", range(40))
-def test_balanced_schedule_invariants(seed, nwc):
+def test_balanced_schedule_invariants(seed, nwc, K):
     rng = np.random.default_rng(seed)
     B = int(rng.choice([1, 2, 3, 7, 31, 64, 255, 256, 257, 600, 2048]))
     kind = seed % 4
@@ -89,17 +101,37 @@ def test_balanced_schedule_invariants(seed, nwc):
         L = np.clip(np.rint(np.exp(rng.normal(7, 1, B))), 16, 16384)
     else:
         L = rng.integers(0, 3, B) * rng.integers(1, 5000, B)  # many zeros
-    _check([int(x) for x in L], nwc)
+    _check([int(x) for x in L], nwc, K)
 
 
-def test_balanced_schedule_edges():
-    _check([0])
-    _check([0, 0, 0])
-    _check([1])
-    _check([16 * 256])          # exactly one tile per workgroup
-    _check([16 * 256 + 1])
-    _check([32768] * 4)
-    _check([4096] * 64)         # every sequence in four pieces
+@pytest.mark.parametrize("K", [0, K_LIB])
+def test_balanced_schedule_edges(K):
+    _check([0], K=K)
+    _check([0, 0, 0], K=K)
+    _check([1], K=K)
+    _check([16 * 256], K=K)          # one tile per workgroup (K = 0)
+    _check([16 * 256 + 1], K=K)
+    _check([32768] * 4, K=K)
+    _check([4096] * 64, K=K)         # every sequence in four pieces (K = 0)
+    _check([16] * 2048, K=K)         # one tile each: K + 1 positions a sequence
+    _check([16, 0, 5000, 17, 0, 0, 33] * 50, nwc=768, K=K)
+
+
+def test_sequence_start_charge_evens_out_the_shares():
+    """Shares that start more sequences hold fewer tiles: on a lognormal
+    length mix, tiles + K x pieces spreads less across the shares than the
+    tiles alone do with K = 0."""
+    rng = np.random.default_rng(5)
+    L = [int(x) for x in np.clip(np.rint(np.exp(rng.normal(7, 1, 128))), 16, 16384)]
+
+    def spread(K):
+        pieces, _, NW = schedule(L, 384, K)
+        load = np.zeros(NW)
+        for wi, b, a, e, slot in pieces:
+            load[wi] += (e - a) + K_LIB  # time in tiles: a start costs about K_LIB
+        return load.max() - load.mean()
+
+    assert spread(K_LIB) < 0.6 * spread(0)
 
 
 # --- shared-prefix decode: the grouped prefix work ---------------------------
@@ -110,11 +142,11 @@ def test_balanced_schedule_edges():
 # workgroup order) takes piece gw // U of unit gw % U, U = Hkv * row_groups;
 # a unit is (row group, kv head) with the kv head fastest, and column n of
 # row group rg is row rg * 16 + n of the kv head's rows, sequence-major.  The
-# prefix is cut into pieces of a multiple of 16 tokens, about 512 each.
+# prefix is cut into pieces of a multiple of 16 tokens, about 384 each.
 # The decode shares give up the grouped rows of workgroups, so the grid is
 # resident at once (at least a quarter of the shares stay).
 
-GROUP_TOKENS = 512
+GROUP_TOKENS = 384
 
 
 def grouped_plan(B, Hq, Hkv, P, waves, chunks, workgroups):
