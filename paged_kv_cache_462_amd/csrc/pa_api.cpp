@@ -132,7 +132,14 @@ constexpr int kSinglePassMaxTokens = 256;
 
 // balanced_only: the automatic plan is always the balanced schedule (the
 // shared-prefix decode needs it), whatever the context length.
-// Tiles' worth of time charged for each sequence a balanced share starts.
+// Tiles' worth of time charged for each sequence a balanced share starts,
+// in the decode of the rest after a shared prefix.  A piece's start costs a
+// wave about three tiles' time (3 to 4 us against 0.8 to 1.2 us a tile,
+// measured on the shared-prompt batches), and the rest of each sequence is
+// short, so shares hold several pieces; the charge gives the shares that
+// start more sequences fewer tiles.  Plain decode deals equal shares of
+// tiles: with equal lengths they fall on sequence boundaries, which the
+// charge would shift (the 70B-shaped batch measured 0.6 % slower with it).
 constexpr int kPieceCost = 3;
 
 int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out,
@@ -302,11 +309,6 @@ int decode_setup(pa_tensor* out, const pa_tensor* query, const pa_tensor* key_ca
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
   p.split = plan.split;
-  // a piece's start costs a wave about three tiles' time (measured on the
-  // shared-prompt and lognormal-length batches: 3 to 4 us a piece against
-  // 0.8 to 1.2 us a tile); charging it in the deal shortens the shares
-  // that start several sequences
-  p.piece_cost = plan.sched == pa::kSchedBalanced ? kPieceCost : 0;
   const double ks = kvdt == PA_FP8_E4M3 ? (double)key_cache->scale : 1.0;
   p.qk_scale_log2 = (float)((double)scale * ks * 1.4426950408889634);
   p.v_scale = kvdt == PA_FP8_E4M3 ? value_cache->scale : 1.0f;
@@ -535,6 +537,7 @@ int pa_decode_shared_prefix(pa_tensor* out, const pa_tensor* query, const pa_ten
   p.skip = prefix_tokens;
   p.prefix_pieces = pp.pieces;
   p.prefix_slot0 = (int32_t)plan.slots;
+  p.piece_cost = kPieceCost;
   hipStream_t stream = static_cast<hipStream_t>(ln.stream);
   hipError_t e;
   if (pp.pass) {

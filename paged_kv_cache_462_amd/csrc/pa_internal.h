@@ -70,7 +70,8 @@ struct DecodeParams {
   int32_t prefix_slot0;
   int32_t* flags;         // caller's error flags [kNumFlags], or null
   // Balanced schedule: the cost, in tiles, charged for the start of every
-  // non-empty sequence when the shares are dealt (0: shares of equal tiles)
+  // non-empty sequence when the shares are dealt (0: shares of equal tiles;
+  // the shared-prefix decode charges 3)
   int32_t piece_cost;
   // Grouped prefix work of a shared-prefix decode (matrix-core kernel,
   // balanced schedule): grp_y more rows of workgroups after the nwc decode

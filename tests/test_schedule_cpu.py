@@ -8,7 +8,8 @@ and NW = min(nwc, T / (K + 1)) (nwc: 256 / unit chunks for 8-wave
 workgroups, 768 / unit chunks for the fp8 kernel's 4-wave ones).  A tile
 belongs to the share that holds its position, and piece k of sequence b gets
 the triple slot owner(S_b + K) + b + k.  These checks hold that arithmetic to
-its invariants on many length mixes, grid sizes and K (3 is the library's):
+its invariants on many length mixes, grid sizes and K (plain decode deals
+with K = 0, the decode of the rest after a shared prefix with K = 3):
 every tile is covered once, the pieces of a sequence go to consecutive
 workgroups, every share holds a tile, and slots are unique and below
 768 + B (the workspace size pa_decode_plan reports)."""
@@ -19,7 +20,7 @@ import pytest
 TILE = 16
 NWC = 256
 SLOTS = 768   # shares per unit chunk the workspace holds slots for
-K_LIB = 3     # the library's charge for a sequence start
+K_LIB = 3     # the shared-prefix decode's charge for a sequence start (plain decode: 0)
 
 
 def schedule(lengths, nwc=NWC, K=K_LIB):
