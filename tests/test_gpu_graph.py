@@ -72,11 +72,21 @@ def test_prefill_graph_replay():
                                 wl.scale, c.block_size, c.num_kv_heads), out)
 
 
-def test_shared_prefix_graph_replay():
-    cfg = shrink(get_config("c3"), batch=5, lengths=("list", [300, 256, 900, 40, 512]),
-                 shared_prefix_tokens=256)
+SHARED = {
+    # 5 x 8 rows per kv head: the grouped prefix work inside the decode launch
+    "grouped": [300, 256, 900, 40, 512],
+    # 130 x 8 = 1040 rows: the prefix pass, then the decode of the rest
+    "pass": [int(x) for x in np.random.default_rng(55).integers(0, 600, 130)],
+}
+
+
+@pytest.mark.parametrize("way", list(SHARED))
+def test_shared_prefix_graph_replay(way):
+    lens = SHARED[way]
+    cfg = shrink(get_config("c3"), batch=len(lens), lengths=("list", lens),
+                 shared_prefix_tokens=256, pool_blocks=0)
     wl = make_workload(cfg, seed=54)
-    G.say("graph: shared-prefix decode")
+    G.say(f"graph: shared-prefix decode, {way}")
     d = G.to_device(wl)
     c = wl.cfg
     pb = torch.from_numpy(wl.shared_blocks.astype(np.int32)).to(d.kc.device)
