@@ -40,6 +40,15 @@ CASES = {
                               [int(x) for x in np.random.default_rng(5).integers(0, 1500, 260)]),
     "fp8_f16q_g4": (shrink(get_config("c5"), q_dtype="f16", block_size=16, shared_prefix_tokens=0),
                     160, [161, 159, 640, 1]),
+    # groups that do not divide the 16 query columns: a row group holds the
+    # end of one sequence's heads and the start of the next one's
+    "bf16_g5_3kv": (shrink(get_config("c3"), num_q_heads=15, num_kv_heads=3), 128,
+                    [5, 130, 128, 400, 0, 77, 129]),
+    "fp8_g12_2kv_d64": (shrink(get_config("c5"), num_q_heads=24, num_kv_heads=2, head_dim=64,
+                               shared_prefix_tokens=0), 64, [64, 63, 65, 500, 1]),
+    # 205 x 5 = 1025 rows per kv head: the prefix pass with odd shapes
+    "bf16_g5_3kv_pass": (shrink(get_config("c3"), num_q_heads=15, num_kv_heads=3), 256,
+                         [int(x) for x in np.random.default_rng(6).integers(0, 450, 205)]),
 }
 
 
