@@ -179,3 +179,63 @@ def test_copy_blocks_flags_pairs_outside_the_pool():
     assert _raised(flags) == {BLOCK}
     k0[2], v0[2] = k0[1], v0[1]
     assert torch.equal(kc, k0) and torch.equal(vc, v0)
+
+
+# sequence 3 is the longest, 608 tokens: the whole table, so its length
+# clamped from a value past the table's reach reads real tokens
+SHARED = {
+    # 6 x 8 rows per kv head: the grouped prefix work in the decode launch
+    "grouped": [300, 200, 256, 608, 512, 60],
+    # 130 x 8 = 1040 rows: the prefix pass
+    "pass": [int(x) for x in np.random.default_rng(99).integers(0, 600, 130)],
+}
+SHARED["pass"][3] = 608
+
+
+@pytest.mark.parametrize("way", list(SHARED))
+def test_shared_prefix_with_bad_prefix_ids_and_lengths(way):
+    """pa_decode_shared_prefix reads the prefix through its own block list:
+    ids there outside the pool read block 0 and raise the block-id flag, as
+    lengths outside the table's reach raise the length flag; the result is
+    the oracle's on the contents taken that way (the prefix part of every
+    sequence from the clamped list, the rest from its own table)."""
+    P = 256
+    lens = SHARED[way]
+    cfg = shrink(get_config("c3"), batch=len(lens), lengths=("list", lens),
+                 shared_prefix_tokens=P, pool_blocks=0)
+    wl = make_workload(cfg, seed=90)
+    bs = cfg.block_size
+    assert wl.max_blocks * bs == lens[3]
+    kc, vc = G.oracle_caches(wl)
+    d = G.to_device(wl)
+    src = int(wl.block_tables[0, 0])
+    kc[0], vc[0] = kc[src].clone(), vc[src].clone()
+    d.kc[0], d.vc[0] = d.kc[src].clone(), d.vc[src].clone()
+    pref = wl.shared_blocks.astype(np.int64).copy()
+    pref[1] = wl.num_blocks + 3
+    pref[4] = -2
+    lens2 = wl.seq_lens.copy()
+    lens2[3] = 10**6
+    lens2[5] = -1
+    d.lens = torch.from_numpy(lens2).to(d.kc.device)
+    G.say(f"untrusted shared prefix {way}: B={cfg.batch}")
+    clean = type(wl)(**{**wl.__dict__})
+    cl = np.clip(lens2, 0, wl.max_blocks * bs).astype(np.int32)
+    clean.seq_lens = cl
+    ids = np.where((pref < 0) | (pref >= wl.num_blocks), 0, pref)
+    t2 = wl.block_tables.copy()
+    for b in range(cfg.batch):
+        nb = -(-min(int(cl[b]), P) // bs)
+        t2[b, :nb] = ids[:nb]
+    clean.block_tables = t2.astype(np.int32)
+    ref = G.oracle_decode(clean, kc, vc)
+    assert not np.isnan(ref).any()
+    out = torch.empty_like(d.query)
+    flags = _flags()
+    pb = torch.from_numpy(pref.astype(np.int32)).to(d.kc.device)
+    pa.decode_shared_prefix(out, d.query, d.kc, d.vc, d.tables, d.lens, pb, P, wl.scale, bs,
+                            cfg.num_kv_heads, error_flags=flags)
+    torch.cuda.synchronize()
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(out, ref, atol, rtol, what=f"untrusted shared prefix {way}")
+    assert _raised(flags) == {BLOCK, LENGTH}
