@@ -6,6 +6,7 @@ alone."""
 
 import threading
 
+import numpy as np
 import pytest
 import torch
 
@@ -155,3 +156,52 @@ def test_side_stream_without_workspace():
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(_bits(o), _bits(ref))
+
+
+def _shared_job(lens, seed, P=256):
+    cfg = shrink(get_config("c3"), batch=len(lens), lengths=("list", lens),
+                 shared_prefix_tokens=P, pool_blocks=0)
+    wl = make_workload(cfg, seed=seed)
+    c = wl.cfg
+    d = G.to_device(wl)
+    pb = torch.from_numpy(wl.shared_blocks.astype(np.int32)).to(d.kc.device)
+    need = pa.decode_shared_prefix_workspace_bytes(c.batch, c.num_q_heads, c.num_kv_heads,
+                                                   c.head_dim, c.block_size, wl.max_blocks, P)
+    ws = torch.empty(need, dtype=torch.uint8, device=d.kc.device)
+
+    def run(out, stream=None):
+        pa.decode_shared_prefix(out, d.query, d.kc, d.vc, d.tables, d.lens, pb, P, wl.scale,
+                                c.block_size, c.num_kv_heads, workspace=ws, stream=stream)
+    return d, run
+
+
+def test_shared_prefix_beside_decode_on_streams():
+    """Both ways of the shared-prefix call (the grouped work in the decode
+    launch; the prefix pass, then the decode of the rest) on two streams
+    while a plain decode runs on a third, several rounds: every result is
+    the bits of the same call alone."""
+    G.say("streams: shared-prefix calls beside a decode")
+    rng = np.random.default_rng(65)
+    jobs = [_shared_job([300, 900, 256, 40, 1200, 0], 66),
+            _shared_job([int(x) for x in rng.integers(0, 700, 130)], 67)]
+    _, dd, drun = _decode_job(shrink(get_config("c3"), batch=8, lengths=("uniform", 100, 3000),
+                                     pool_blocks=0), 68)
+    ref = [torch.empty_like(d.query) for d, _ in jobs]
+    for (_, run), o in zip(jobs, ref):
+        run(o)
+    dref = torch.empty_like(dd.query)
+    drun(dref)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = [[torch.empty_like(d.query) for d, _ in jobs] for _ in range(3)]
+    douts = [torch.empty_like(dd.query) for _ in range(3)]
+    torch.cuda.current_stream().synchronize()
+    for r in range(3):
+        for (_, run), o, s in zip(jobs, outs[r], streams):
+            run(o, stream=s)
+        drun(douts[r], stream=streams[2])
+    torch.cuda.synchronize()
+    for r in range(3):
+        for o, e in zip(outs[r], ref):
+            assert torch.equal(_bits(o), _bits(e))
+        assert torch.equal(_bits(douts[r]), _bits(dref))
