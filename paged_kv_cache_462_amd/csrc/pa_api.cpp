@@ -130,8 +130,6 @@ int flags_of(const pa_launch* launch, int32_t** out) {
 // chunk) walks them in about the time a second (merge) launch would take.
 constexpr int kSinglePassMaxTokens = 256;
 
-// balanced_only: the automatic plan is always the balanced schedule (the
-// shared-prefix decode needs it), whatever the context length.
 // Tiles' worth of time charged for each sequence a balanced share starts,
 // in the decode of the rest after a shared prefix.  A piece's start costs a
 // wave about three tiles' time (3 to 4 us against 0.8 to 1.2 us a tile,
@@ -142,6 +140,8 @@ constexpr int kSinglePassMaxTokens = 256;
 // charge would shift (the 70B-shaped batch measured 0.6 % slower with it).
 constexpr int kPieceCost = 3;
 
+// balanced_only: the automatic plan is always the balanced schedule (the
+// shared-prefix decode needs it), whatever the context length.
 int make_plan(int B, int Hq, int Hkv, int D, int bs, int max_blocks, int req, Plan* out,
               bool balanced_only = false) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0)
