@@ -139,3 +139,47 @@ def test_prefix_cache_chain_full_size(name):
         ch.manager.free_sequence(sid)
     ch.cache.evict(wl.num_blocks)
     assert ch.cache.size() == 0 and ch.alloc.num_free() == wl.num_blocks
+
+
+def _random_case(seed):
+    """A seeded shape: dtype pair, head_dim, block size, group, prefix
+    length and a length mix around the prefix, with B * G on either side
+    of the 1024 rows where the prefix part changes ways."""
+    rng = np.random.default_rng(seed)
+    q, kv = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8"), ("f16", "fp8")][seed % 4]
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32]))
+    Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 5, 8, 16]))
+    B = int(rng.integers(1, 40)) if seed % 3 else int(-(-1100 // G))  # many rows every third case
+    P = bs * int(rng.integers(1, 1 + 640 // bs))
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        lens = rng.integers(0, 2 * P + 64, B)
+    elif kind == 1:
+        lens = P + rng.integers(-bs, 3 * bs, B)
+    else:
+        lens = rng.integers(0, P + 1, B)
+    lens = np.maximum(lens, 0)
+    lens[0] = max(int(lens[0]), P)  # the tables reach the whole prefix
+    base = get_config("c5") if kv == "fp8" else get_config("c3")
+    cfg = shrink(base, batch=B, num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                 q_dtype=q, kv_dtype=kv, lengths=("list", [int(x) for x in lens]),
+                 shared_prefix_tokens=P, pool_blocks=0)
+    return cfg, P
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_shared_prefix_random_shapes(seed):
+    cfg, P = _random_case(seed)
+    wl = make_workload(cfg, seed=700 + seed)
+    G.say(f"shared prefix random {seed}: B={cfg.batch} Hq={cfg.num_q_heads} Hkv={cfg.num_kv_heads} "
+          f"D={cfg.head_dim} bs={cfg.block_size} {cfg.q_dtype}/{cfg.kv_dtype} P={P} "
+          f"rows={cfg.batch * cfg.num_q_heads // cfg.num_kv_heads}")
+    kc, vc = G.oracle_caches(wl)
+    ref = G.oracle_decode(wl, kc, vc)
+    d = G.to_device(wl)
+    out = _run(wl, P, d)
+    torch.cuda.synchronize()
+    atol, rtol = G.tol_for(wl)
+    G.assert_close(out, ref, atol, rtol, what=f"shared prefix random {seed}")
